@@ -1,0 +1,364 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics fix,
+never against the oracle's own formulas retyped.  CPU only."""
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from workloads import configs as C
+from workloads import generate as G
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+F32 = np.float32
+
+
+# ------------------------------------------------------------------ helpers
+def fp32_nearest(fr: Fraction) -> np.float32:
+    """The fp32 nearest to an exact rational (ties to even), by exact comparison of neighbours."""
+    r = np.float32(float(fr))
+    cands = [np.nextafter(r, F32(-np.inf)), r, np.nextafter(r, F32(np.inf))]
+    best = min(cands, key=lambda c: (abs(Fraction(float(c)) - fr),
+                                     int(np.array(c, dtype=F32).view(np.uint32)) & 1))
+    return F32(best)
+
+
+def rand_small_cfg(**kw):
+    base = dict(name="pin", num_tokens=40, hidden=64, num_experts=16, top_k=4, intermediate=32,
+                num_shared=1, shared_intermediate=16, recipe=C.RECIPE_F32)
+    base.update(kw)
+    return C.MoEConfig(**base)
+
+
+def brute_select(key_row, n_group, topk_group, k):
+    """Selection by full sorts of Python tuples (page: group top-2 sums, keep groups, top-k)."""
+    E = len(key_row)
+    keys = [float(v) for v in key_row]
+    if n_group > 1:
+        gs = E // n_group
+        gscores = []
+        for g in range(n_group):
+            members = sorted(keys[g * gs:(g + 1) * gs], reverse=True)
+            gscores.append((-float(F32(members[0]) + F32(members[1])), g))
+        kept_groups = {g for _, g in sorted(gscores)[:topk_group]}
+        cand = [e for e in range(E) if e // gs in kept_groups]
+    else:
+        cand = list(range(E))
+    return [e for _, e in sorted((-keys[e], e) for e in cand)[:k]]
+
+
+# ------------------------------------------------------------------ score functions
+def test_score_closed_forms():
+    z = np.array([0.0], dtype=F32)
+    assert O.score(z, O.SCORE_SIGMOID)[0] == F32(0.5)
+    # sqrt(softplus(0)) = sqrt(ln 2) = 0.83255461115769775...
+    assert O.score(z, O.SCORE_SQRTSOFTPLUS)[0] == F32(0.8325546111576977)
+    # large z: softplus(z) -> z, so sqrtsoftplus(z) -> sqrt(z); sigmoid -> 1
+    big = np.array([60.0, 100.0], dtype=F32)
+    assert np.array_equal(O.score(big, O.SCORE_SQRTSOFTPLUS), np.sqrt(big.astype(np.float64)).astype(F32))
+    assert np.all(O.score(big, O.SCORE_SIGMOID) == F32(1.0))
+    # very negative: sigmoid(z) ~ e^z, sqrtsoftplus(z) ~ e^(z/2)
+    neg = np.array([-40.0], dtype=F32)
+    assert O.score(neg, O.SCORE_SIGMOID)[0] == F32(math.exp(-40.0))
+    assert O.score(neg, O.SCORE_SQRTSOFTPLUS)[0] == F32(math.exp(-20.0))
+
+
+def test_score_monotone():
+    z = np.sort(np.random.default_rng(1).standard_normal(5000).astype(F32) * 8)
+    for f in (O.SCORE_SIGMOID, O.SCORE_SQRTSOFTPLUS):
+        s = O.score(z, f)
+        assert np.all(np.diff(s.astype(np.float64)) >= 0)
+
+
+def test_score_correctly_rounded_decimal():
+    getcontext().prec = 60
+    rng = np.random.default_rng(2)
+    z = (rng.standard_normal(400) * 3).astype(F32)
+    sig = O.score(z, O.SCORE_SIGMOID)
+    ssp = O.score(z, O.SCORE_SQRTSOFTPLUS)
+    for zi, a, b in zip(z, sig, ssp):
+        d = Decimal(float(zi))
+        exact_sig = 1 / (1 + (-d).exp())
+        exact_ssp = (1 + d.exp()).ln().sqrt()
+        for got, exact in ((a, exact_sig), (b, exact_ssp)):
+            fr = Fraction(exact)
+            assert fp32_nearest(fr) == got, (zi, got)
+
+
+# ------------------------------------------------------------------ logits
+def test_logits_are_correctly_rounded_dot_products():
+    rng = np.random.default_rng(3)
+    T, E, H = 12, 10, 96
+    x = rng.standard_normal((T, H)).astype(F32)
+    # bf16-valued x as in the bf16 recipes: keep the top 16 bits
+    xb = (x.view(np.uint32) & 0xFFFF0000).view(F32)
+    w = (rng.standard_normal((E, H)) * 0.1).astype(F32)
+    for xx in (x, xb):
+        got = O.gate_logits(xx.astype(np.float64), w.astype(np.float64))
+        for t in range(T):
+            for e in range(E):
+                exact = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(xx[t], w[e]))
+                assert got[t, e] == fp32_nearest(exact)
+
+
+# ------------------------------------------------------------------ selection
+@pytest.mark.parametrize("E,n_group,topk_group,k", [(16, 1, 1, 4), (32, 4, 2, 6), (32, 8, 4, 8),
+                                                    (24, 3, 1, 5), (64, 8, 3, 8)])
+def test_topk_matches_bruteforce(E, n_group, topk_group, k):
+    cfg = rand_small_cfg(num_experts=E, top_k=k, n_group=n_group, topk_group=topk_group)
+    rng = np.random.default_rng(E + k)
+    T, H = 50, 64
+    x = rng.standard_normal((T, H))
+    wg = rng.standard_normal((E, H)) / 8
+    b = (rng.uniform(-0.1, 0.1, E)).astype(F32)
+    r = O.route(cfg, x, wg, b)
+    for t in range(T):
+        assert list(r["idx"][t]) == brute_select(r["key"][t], n_group, topk_group, k)
+
+
+def test_group_step_is_identity_when_one_group_or_all_groups_kept():
+    rng = np.random.default_rng(5)
+    T, H, E, k = 60, 64, 32, 6
+    x = rng.standard_normal((T, H)); wg = rng.standard_normal((E, H)) / 8
+    b = rng.uniform(-0.1, 0.1, E).astype(F32)
+    plain = rand_small_cfg(num_experts=E, top_k=k)
+    ref = O.route(plain, x, wg, b)["idx"]
+    # plain top-k written as a full argsort of (-key, index)
+    key = O.route(plain, x, wg, b)["key"]
+    for t in range(T):
+        assert list(ref[t]) == [e for _, e in sorted((-float(v), e) for e, v in enumerate(key[t]))][:k]
+    allkept = rand_small_cfg(num_experts=E, top_k=k, n_group=4, topk_group=4)
+    assert np.array_equal(O.route(allkept, x, wg, b)["idx"], ref)
+
+
+def test_exact_ties_go_to_lowest_index():
+    T, H, E, k = 8, 32, 16, 4
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((T, H))
+    row = rng.standard_normal(H) / 8
+    wg = np.tile(row, (E, 1))                       # every expert has the same gate row
+    b = np.zeros(E, dtype=F32)
+    r = O.route(rand_small_cfg(num_experts=E, top_k=k), x, wg, b)
+    assert np.all(r["idx"] == np.arange(k))
+    rg = O.route(rand_small_cfg(num_experts=E, top_k=k, n_group=4, topk_group=2), x, wg, b)
+    assert np.all(rg["idx"] == np.arange(k))         # groups 0, 1 kept; experts 0..3
+    # twins at the boundary: experts 9 and 3 have identical gate rows and bias;
+    # whenever only one of them makes the cut it must be 3
+    T2 = 64
+    x2 = rng.standard_normal((T2, H))
+    wg2 = rng.standard_normal((E, H)) / 8
+    wg2[9] = wg2[3]
+    b2 = np.full(E, -5.0, dtype=F32); b2[[1, 3, 9, 12]] = 5.0; b2[5] = 6.0
+    r2 = O.route(rand_small_cfg(num_experts=E, top_k=4), x2, wg2, b2)
+    only_one = 0
+    for t in range(T2):
+        sel = set(r2["idx"][t].tolist())
+        assert 5 in sel
+        assert (9 not in sel) or (3 in sel)
+        only_one += (3 in sel) and (9 not in sel)
+    assert only_one > 0
+
+
+# ------------------------------------------------------------------ weights
+@pytest.mark.parametrize("func,scale", [(O.SCORE_SIGMOID, 2.827), (O.SCORE_SQRTSOFTPLUS, 2.5)])
+def test_weights_sum_to_scale_and_positive(func, scale):
+    rng = np.random.default_rng(7)
+    cfg = rand_small_cfg(num_experts=32, top_k=8, score_func=func, routed_scaling_factor=scale)
+    x = rng.standard_normal((100, 64)); wg = rng.standard_normal((32, 64)) / 8
+    b = rng.normal(0, 0.01, 32).astype(F32)
+    w = O.route(cfg, x, wg, b)["w"].astype(np.float64)
+    assert np.all(w > 0)
+    assert np.all(np.abs(w.sum(axis=1) - scale) <= 8 * 2.0 ** -23 * scale)
+
+
+def test_forcing_bias_selects_and_weights_use_unbiased_scores():
+    rng = np.random.default_rng(8)
+    E, k, H, T = 16, 4, 64, 30
+    x = rng.standard_normal((T, H)); wg = rng.standard_normal((E, H)) / 8
+    b = np.zeros(E, dtype=F32); b[:k] = 10.0
+    cfg = rand_small_cfg(num_experts=E, top_k=k, routed_scaling_factor=2.827)
+    r = O.route(cfg, x, wg, b)
+    for t in range(T):
+        assert sorted(r["idx"][t].tolist()) == list(range(k))
+        # weights proportional to sigma(logit) of the chosen experts, not to sigma + 10
+        z = np.array([float(np.dot(x[t], wg[e])) for e in r["idx"][t]])
+        sig = 1 / (1 + np.exp(-z))
+        np.testing.assert_allclose(r["w"][t], sig / sig.sum() * 2.827, rtol=2e-6)
+
+
+# ------------------------------------------------------------------ permutation
+def test_permutation_invariants_and_round_trip():
+    rng = np.random.default_rng(9)
+    T, k, E = 257, 6, 40
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    for t in range(50):                                # a popular expert (no token picks it twice)
+        if 3 not in idx[t]:
+            idx[t, 0] = 3
+    p = O.permute(idx, E)
+    assert p["counts"].sum() == T * k
+    assert p["offsets"][0] == 0 and np.array_equal(np.diff(p["offsets"]), p["counts"])
+    assert np.array_equal(np.sort(p["sorted_pair"]), np.arange(T * k))          # bijection
+    flat = idx.reshape(-1)
+    for e in range(E):
+        blk = p["sorted_pair"][p["offsets"][e]:p["offsets"][e + 1]]
+        assert np.all(flat[blk] == e)                                           # contiguous block
+        assert np.all(np.diff(blk // k) > 0)                                   # ascending tokens
+    rows = np.arange(T * k)[p["sorted_pair"]]          # permute...
+    assert np.array_equal(rows[p["pair_pos"]], np.arange(T * k))               # ...and back
+    # un-permute of data rows restores original order exactly
+    data = rng.standard_normal((T * k, 3))
+    assert np.array_equal(data[p["sorted_pair"]][p["pair_pos"]], data)
+
+
+# ------------------------------------------------------------------ FFN
+def _loops_mlp(x, w13, w2):
+    I = len(w13) // 2
+    out = []
+    for row in x:
+        h = []
+        for i in range(I):
+            g = sum(a * b for a, b in zip(row, w13[i]))
+            u = sum(a * b for a, b in zip(row, w13[I + i]))
+            h.append(g / (1 + math.exp(-g)) * u)
+        out.append([sum(a * b for a, b in zip(h, w2[n])) for n in range(len(w2))])
+    return np.array(out)
+
+
+def test_expert_mlp_matches_scalar_loops():
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((3, 8)); w13 = rng.standard_normal((8, 8)); w2 = rng.standard_normal((8, 4))
+    np.testing.assert_allclose(O.expert_mlp(x, w13, w2), _loops_mlp(x, w13, w2), rtol=1e-12, atol=1e-12)
+
+
+def _f32_raw(w13, w2):
+    return lambda e: {"w13": w13[e], "w2": w2[e]}
+
+
+def test_single_expert_layer_is_textbook_swiglu():
+    rng = np.random.default_rng(11)
+    T, H, I = 5, 8, 6
+    cfg = rand_small_cfg(num_tokens=T, hidden=H, num_experts=1, top_k=1, intermediate=I,
+                         shared_intermediate=4, routed_scaling_factor=1.0)
+    x = rng.standard_normal((T, H)); wg = rng.standard_normal((1, H))
+    w13 = rng.standard_normal((1, 2 * I, H)).astype(F32); w2 = rng.standard_normal((1, H, I)).astype(F32)
+    s13 = rng.standard_normal((1, 8, H)); s2 = rng.standard_normal((1, H, 4))
+    r = O.moe_forward(cfg, x, wg, np.zeros(1, F32), _f32_raw(w13, w2), s13, s2)
+    want = _loops_mlp(x, w13[0].astype(np.float64), w2[0].astype(np.float64)) + _loops_mlp(x, s13[0], s2[0])
+    np.testing.assert_allclose(r["out"], want, rtol=1e-12, atol=1e-12)
+
+
+def test_sparse_layer_equals_dense_bruteforce():
+    rng = np.random.default_rng(12)
+    T, H, E, k, I = 7, 16, 8, 3, 8
+    cfg = rand_small_cfg(num_tokens=T, hidden=H, num_experts=E, top_k=k, intermediate=I,
+                         num_shared=2, shared_intermediate=4, n_group=2, topk_group=1,
+                         routed_scaling_factor=2.827)
+    x = rng.standard_normal((T, H)); wg = rng.standard_normal((E, H)) / 4
+    b = rng.uniform(-0.1, 0.1, E).astype(F32)
+    w13 = rng.standard_normal((E, 2 * I, H)).astype(F32); w2 = rng.standard_normal((E, H, I)).astype(F32)
+    s13 = rng.standard_normal((2, 8, H)); s2 = rng.standard_normal((2, H, 4))
+    r = O.moe_forward(cfg, x, wg, b, _f32_raw(w13, w2), s13, s2)
+    dense_w = np.zeros((T, E))
+    np.put_along_axis(dense_w, r["routing"]["idx"].astype(np.int64), r["routing"]["w"].astype(np.float64), 1)
+    want = np.zeros((T, H))
+    for e in range(E):                                  # every expert on every token
+        want += dense_w[:, e:e + 1] * _loops_mlp(x, w13[e].astype(np.float64), w2[e].astype(np.float64))
+    for s in range(2):
+        want += _loops_mlp(x, s13[s], s2[s])
+    np.testing.assert_allclose(r["out"], want, rtol=1e-11, atol=1e-11)
+
+
+# ------------------------------------------------------------------ number formats
+def test_e2m1_grid_and_e8m0():
+    codes = np.arange(16, dtype=np.uint8)
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    v = O.decode_e2m1_packed(packed[None])[0]
+    assert list(v[:8]) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert list(v[8:]) == [-0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+    e8 = O.decode_e8m0(np.array([0, 126, 127, 128, 254, 255], dtype=np.uint8))
+    assert list(e8[:5]) == [2.0 ** -127, 0.5, 1.0, 2.0, 2.0 ** 127] and math.isnan(e8[5])
+
+
+def test_e4m3_decode_matches_torch_and_max_is_448():
+    codes = np.arange(256, dtype=np.uint8)
+    t = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    o = O.decode_e4m3(codes)
+    assert np.array_equal(np.isnan(t), np.isnan(o)) and np.array_equal(t[~np.isnan(t)], o[~np.isnan(o)])
+    assert np.nanmax(o) == 448.0 and np.isnan(o[0x7F]) and np.isnan(o[0xFF])
+
+
+def test_e4m3_encode_matches_torch_cast():
+    rng = np.random.default_rng(13)
+    mids = O._E4M3_MID
+    v = np.concatenate([rng.standard_normal(200000) * 64, rng.standard_normal(20000) * 1e-2,
+                        mids, -mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9),
+                        [0.0, -0.0, 1e-12, -1e-12, 448.0, -448.0]]).astype(F32)
+    v = np.clip(v, -448, 448)
+    want = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.encode_e4m3(v), want)
+
+
+def test_every_e2m1_value_is_exact_in_e4m3():
+    """FP4 -> FP8 conversion (e2m1fn -> e4m3fn) is lossless; checked through the oracle's codecs."""
+    page = json.load(open(os.path.join(HERE, "golden", "page_constants.json")))
+    assert page["e2m1_to_e4m3_lossless"]["value"] is True
+    e2m1 = O.E2M1_TABLE
+    for scale_exp in range(-6, 4):                     # with any power-of-two block scale in range
+        v = e2m1 * 2.0 ** scale_exp
+        back = O.decode_e4m3(O.encode_e4m3(v))
+        assert np.array_equal(back, v)
+
+
+def test_mx_exponent_is_least_that_fits():
+    rng = np.random.default_rng(14)
+    a = np.abs(rng.standard_normal(20000)) * 10.0 ** rng.uniform(-6, 6, 20000)
+    a = np.concatenate([a, 448.0 * 2.0 ** np.arange(-20, 20)])       # exact powers on the edge
+    e = O.mx_exponent(a, 448.0)
+    assert np.all(a <= 448.0 * np.ldexp(1.0, e))
+    assert np.all(a > 448.0 * np.ldexp(1.0, e - 1))
+
+
+def test_activation_quantisers_bound_and_round_trip():
+    rng = np.random.default_rng(15)
+    v = (rng.standard_normal((9, 256)) * 3).astype(F32)
+    v[2, :128] = 0.0                                   # an all-zero block
+    q, s = O.quant_fp8_b128(v)
+    assert s[2, 0] == 1.0 and np.all(q[2, :128] & 0x7F == 0)
+    d = O.dequant_fp8_b128(q, s)
+    assert np.all(np.abs(d - v) <= np.abs(v) * 2.0 ** -4 + s.repeat(128, 1) * 2.0 ** -10)
+    assert np.all(np.abs(O.decode_e4m3(q)) <= 448.0)
+    # quantising the dequantised values again gives the same codes (Q(D(q)) = q)
+    q2, s2 = O.quant_fp8_b128(d.astype(F32))
+    assert np.array_equal(q2, q) and np.array_equal(s2, s)
+    qm, em = O.quant_mxfp8(v)
+    dm = O.dequant_mxfp8(qm, em)
+    assert np.all(np.abs(dm - v) <= np.abs(v) * 2.0 ** -4 + O.decode_e8m0(em).repeat(32, 1) * 2.0 ** -9)
+    # dequantised values are exactly representable: quantising them again loses nothing
+    # (codes may differ: a block whose amax rounded down to 224*2^e re-quantises with e - 1)
+    q3, e3 = O.quant_mxfp8(dm.astype(F32))
+    assert np.array_equal(O.dequant_mxfp8(q3, e3), dm)
+
+
+# ------------------------------------------------------------------ page constants
+def test_page_constants_and_mxfp4_byte_accounting():
+    page = json.load(open(os.path.join(HERE, "golden", "page_constants.json")))
+    assert C.DECODE_BF16.routed_scaling_factor == page["routed_scaling_factor_v3"]["value"]
+    assert C.SKEWED_FP8.routed_scaling_factor == page["route_scale_v4"]["value"]
+    v3, v4, k3 = page["v3_experts"], page["v4_experts"], page["k3_experts"]
+    assert (C.DECODE_BF16.num_experts, C.DECODE_BF16.top_k, C.DECODE_BF16.num_shared,
+            C.DECODE_BF16.hidden) == (v3["routed"], v3["top_k"], v3["shared"], v3["hidden"])
+    assert (C.SKEWED_FP8.num_experts, C.SKEWED_FP8.top_k, C.SKEWED_FP8.num_shared) == \
+        (v4["routed"], v4["top_k"], v4["shared"])
+    assert (C.FINEGRAINED_MXFP4.num_experts, C.FINEGRAINED_MXFP4.top_k, C.FINEGRAINED_MXFP4.num_shared) == \
+        (k3["routed"], k3["top_k"], k3["shared"])
+    st = page["mxfp4_storage"]
+    lower = st["params"] * st["bits"] / 8 / 1e12
+    assert abs(lower - st["lower_bound_TB"]) < 0.005
+    with_scales = st["params"] * O.mxfp4_bytes_per_param() / 1e12
+    assert st["lower_bound_TB"] < with_scales < st["stored_TB"]
+    assert st["params"] * 2 / 1e12 >= st["unquantised_16bit_TB_at_least"]

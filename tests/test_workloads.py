@@ -1,0 +1,65 @@
+"""The seeded input generator: weight encoders, determinism, the skewed-load bias.  CPU only."""
+import numpy as np
+import torch
+
+from oracle import moe_oracle as O
+from workloads import configs as C
+from workloads import generate as G
+
+
+def test_generation_is_deterministic():
+    a = G.generate(C.MINI_MXFP4)
+    b = G.generate(C.MINI_MXFP4)
+    for name in ("x", "gate_w", "bias", "w13", "w2", "w13_scale", "w2_scale", "shared_w13", "shared_w2"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+
+
+def test_fp8_block_encoder_round_trip():
+    w = torch.randn(256, 384, generator=torch.Generator().manual_seed(1)) * 0.02
+    q, s = G.encode_fp8_block128(w)
+    d = O.dequant_expert(C.RECIPE_FP8_B128, {"w13": q.numpy(), "w13_scale": s.numpy(),
+                                            "w2": q.numpy(), "w2_scale": s.numpy()}, 128, 384)[0]
+    ref = w.double().numpy()
+    sc = np.repeat(np.repeat(s.double().numpy(), 128, 0), 128, 1)
+    assert np.all(np.abs(d - ref) <= np.abs(ref) * 2.0 ** -4 + sc * 2.0 ** -10)
+    # amax of every block maps to the largest code magnitude 448
+    blk = np.abs(O.decode_e4m3(q.numpy())).reshape(2, 128, 3, 128).max(axis=(1, 3))
+    assert np.all(blk == 448.0)
+
+
+def test_mxfp4_encoder_round_trip_and_scale_rule():
+    g = torch.Generator().manual_seed(2)
+    w = torch.randn(64, 256, generator=g) * 0.02
+    w[3, :32] = 0.0
+    q, e8 = G.encode_mxfp4(w)
+    d = O.dequant_expert(C.RECIPE_MXFP4, {"w13": q.numpy(), "w13_scale": e8.numpy(),
+                                         "w2": q.numpy(), "w2_scale": e8.numpy()}, 32, 256)[0]
+    ref = w.double().numpy()
+    scale = O.decode_e8m0(e8.numpy())
+    amax = np.abs(ref).reshape(64, 8, 32).max(axis=2)
+    nz = amax > 0
+    # least exponent with amax <= 6 * 2^e
+    assert np.all(amax[nz] <= 6 * scale[nz]) and np.all(amax[nz] > 3 * scale[nz])
+    # error at most half of the e2m1 step at that magnitude (steps 0.5 / 1 / 2 below 2 / 4 / 6)
+    a = np.abs(ref) / np.repeat(scale, 32, 1)
+    step = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
+    assert np.all(np.abs(d - ref) <= 0.5 * step * np.repeat(scale, 32, 1) + 1e-30)
+
+
+def test_e2m1_encoder_ties_to_even():
+    v = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -5.0, 6.0, 0.2, 5.1])
+    codes = G.encode_e2m1(v)
+    vals = O.E2M1_TABLE[codes.numpy().astype(np.int64)]
+    assert list(vals) == [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, 0.0, -4.0, 6.0, 0.0, 6.0]
+
+
+def test_zipf_bias_gives_heavy_tailed_load():
+    cfg = C.SKEWED_FP8.replace(num_tokens=2048, hidden=256, gate_std=1.0 / 16)
+    inp = G.generate(cfg, experts=False)
+    x = inp.x.float().double().numpy()
+    r = O.route(cfg, x, inp.gate_w.double().numpy(), inp.bias.numpy())
+    load = np.sort(np.bincount(r["idx"].reshape(-1), minlength=cfg.num_experts))[::-1]
+    T = cfg.num_tokens
+    assert load[0] >= 0.9 * T                      # rank-1 expert sees nearly every token
+    assert load[:10].sum() > 0.3 * T * cfg.top_k   # heavy head
+    assert load[-1] < 0.01 * T                      # long thin tail
