@@ -1,0 +1,122 @@
+// Tile lists for the grouped GEMMs, the fp32 expert MLP (VALU), and the
+// stand-alone weighted put-back sum used when a layer has no shared expert.
+// moe_infer per-expert MLP and put-back: DeepSeek-V3 walk-through
+// (pwwt.cn/news/5781524), section 3.4.
+#include "gemm_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// tiles = {count, e_0, m0_0, e_1, m0_1, ...}: every expert's rows cut into BM-row tiles.
+__global__ __launch_bounds__(1024) void build_tiles(const int32_t* __restrict__ offsets, int E, int BM,
+                                                    int32_t* __restrict__ tiles) {
+  __shared__ int32_t cnt[1024];
+  const int e = threadIdx.x;
+  const int m = (e < E) ? offsets[e + 1] - offsets[e] : 0;
+  const int n = (m + BM - 1) / BM;
+  cnt[e] = n;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = (e >= off) ? cnt[e - off] : 0;
+    __syncthreads();
+    cnt[e] += v;
+    __syncthreads();
+  }
+  const int first = cnt[e] - n;
+  for (int q = 0; q < n; ++q) {
+    tiles[1 + 2 * (first + q)] = e;
+    tiles[2 + 2 * (first + q)] = q * BM;
+  }
+  if (e == 1023) tiles[0] = cnt[1023];
+}
+
+// ---------------------------------------------------------------------------
+// fp32 expert MLP on the vector ALU: one thread per output element, 16 x 16 per block.
+// ---------------------------------------------------------------------------
+constexpr int F32_BM = 16;
+
+template <int MODE>
+__global__ __launch_bounds__(256) void ffn_f32_kernel(GemmArgs g) {
+  TileInfo ti;
+  if (!get_tile(g, F32_BM, ti)) return;
+  const int r = threadIdx.x >> 4;
+  const int col = blockIdx.x * 16 + (threadIdx.x & 15);
+  if (r >= ti.rows || col >= g.N) return;
+  const float* A = static_cast<const float*>(g.A) + size_t(ti.row0 + r) * g.lda;
+  const float* B = static_cast<const float*>(g.B);
+  const int K = g.K, ns = g.nsplit;
+  if (MODE == EPI_SWIGLU) {
+    const int sub = ti.e * g.n_experts_split + col / ns, nl = col % ns;
+    const float* wg = B + size_t(sub) * 2 * ns * K + size_t(nl) * K;
+    const float* wu = wg + size_t(ns) * K;
+    float a0 = 0.0f, a1 = 0.0f;
+    for (int k = 0; k < K; ++k) {
+      a0 = fmaf(A[k], wg[k], a0);
+      a1 = fmaf(A[k], wu[k], a1);
+    }
+    static_cast<float*>(g.out)[size_t(ti.row0 + r) * g.ldo + col] = silu_f32(a0) * a1;
+    return;
+  }
+  float acc = 0.0f;
+  for (int k0 = 0; k0 < K; k0 += ns) {                 // down_proj, one sub-expert at a time
+    const int sub = ti.e * g.n_experts_split + k0 / ns;
+    const float* w = B + size_t(sub) * g.N * ns + size_t(col) * ns;
+    for (int k = 0; k < ns; ++k) acc = fmaf(A[k0 + k], w[k], acc);
+  }
+  if (MODE == EPI_STORE) {
+    static_cast<float*>(g.out)[size_t(ti.row0 + r) * g.ldo + col] = acc;
+  } else {
+    const int t = ti.row0 + r, k = g.topk;
+    const float* Yp = static_cast<const float*>(g.y_perm);
+    for (int j = 0; j < k; ++j)
+      acc += g.topk_w[size_t(t) * k + j] * Yp[size_t(g.pair_pos[size_t(t) * k + j]) * g.ldo + col];
+    static_cast<float*>(g.out)[size_t(t) * g.ldo + col] = acc;
+  }
+}
+
+hipError_t launch_f32(int mode, int m_tiles, const GemmArgs& g, hipStream_t st) {
+  const dim3 grid((g.N + 15) / 16, m_tiles);
+  if (mode == EPI_SWIGLU) ffn_f32_kernel<EPI_SWIGLU><<<grid, 256, 0, st>>>(g);
+  else if (mode == EPI_STORE) ffn_f32_kernel<EPI_STORE><<<grid, 256, 0, st>>>(g);
+  else ffn_f32_kernel<EPI_COMBINE><<<grid, 256, 0, st>>>(g);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// out[t] = sum_j w[t][j] * y_perm[pair_pos[t*k+j]] (no shared expert).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void combine_only(const T* __restrict__ yp, const int32_t* __restrict__ pair_pos,
+                                                    const float* __restrict__ w, int k, int H, T* __restrict__ out) {
+  const int t = blockIdx.x;
+  for (int n = threadIdx.x; n < H; n += 256) {
+    float acc = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const size_t row = size_t(pair_pos[size_t(t) * k + j]) * H;
+      float y;
+      if constexpr (sizeof(T) == 4) y = yp[row + n];
+      else y = bf16_to_f32(yp[row + n]);
+      acc += w[size_t(t) * k + j] * y;
+    }
+    if constexpr (sizeof(T) == 4) out[size_t(t) * H + n] = acc;
+    else out[size_t(t) * H + n] = f32_to_bf16(acc);
+  }
+}
+
+hipError_t launch_combine_only(const moe_config_t& c, const void* y_perm, const int32_t* pair_pos,
+                               const float* topk_w, void* out, hipStream_t st) {
+  if (c.recipe == MOE_RECIPE_F32)
+    combine_only<float><<<c.num_tokens, 256, 0, st>>>(static_cast<const float*>(y_perm), pair_pos, topk_w, c.top_k,
+                                                      c.hidden, static_cast<float*>(out));
+  else
+    combine_only<uint16_t><<<c.num_tokens, 256, 0, st>>>(static_cast<const uint16_t*>(y_perm), pair_pos, topk_w,
+                                                         c.top_k, c.hidden, static_cast<uint16_t*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int BM, int32_t* tiles, hipStream_t st) {
+  build_tiles<<<1, 1024, 0, st>>>(offsets, E, BM, tiles);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,59 @@
+// Tile scheduling shared by the grouped-GEMM kernels.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+enum EpiMode { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_COMBINE = 2 };
+
+// Arguments of one grouped (or dense) GEMM launch.
+//   Grouped mode (tiles != nullptr): tile i covers rows offsets[e] + m0 .. of expert e,
+//   where tiles = {count, e_0, m0_0, e_1, m0_1, ...}.  Dense mode: one expert, rows 0..dense_rows.
+struct GemmArgs {
+  const void* A;            // activations [rows][K] (bf16, fp32 or fp8 codes)
+  const void* A_scale;      // activation scales (fp8: fp32 [rows][K/128]; MX: E8M0 [rows][K/32])
+  int lda;
+  const int32_t* offsets;   // [E+1]
+  const int32_t* tiles;
+  int dense_rows;
+  const void* B;            // weights of expert 0 (see the SwiGLU / down layouts below)
+  const void* B_scale;
+  int K;                    // reduction length
+  int N;                    // output columns (h columns for SwiGLU, hidden for down)
+  int nsplit;               // per-sub-expert width: SwiGLU columns (I or Is), down K-split (I or Is)
+  int n_experts_split;      // number of sub-experts stacked in one launch (shared experts), else 1
+  void* out;                // [rows][N]
+  void* out_scale;          // h scales for the quantised recipes
+  int ldo;
+  // combine epilogue
+  const void* y_perm;
+  const int32_t* pair_pos;
+  const float* topk_w;
+  int topk;
+};
+
+struct TileInfo {
+  int e, row0, rows;
+};
+
+__device__ __forceinline__ bool get_tile(const GemmArgs& g, int BM, TileInfo& ti) {
+  if (g.tiles) {
+    const int tile = blockIdx.y;
+    if (tile >= g.tiles[0]) return false;
+    ti.e = g.tiles[1 + 2 * tile];
+    const int m0 = g.tiles[2 + 2 * tile];
+    ti.row0 = g.offsets[ti.e] + m0;
+    ti.rows = min(BM, g.offsets[ti.e + 1] - ti.row0);
+  } else {
+    ti.e = 0;
+    ti.row0 = blockIdx.y * BM;
+    ti.rows = min(BM, g.dense_rows - ti.row0);
+  }
+  return ti.rows > 0;
+}
+
+// 32x32 MFMA accumulator layout: register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+}  // namespace moe

@@ -1,0 +1,49 @@
+// Internal launchers of the MoE library (host side); every one enqueues on `st`
+// and returns hipGetLastError().
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// Pairs per block of the counting sort.
+constexpr int PERM_CHUNK = 1024;
+
+inline int perm_blocks(int pairs) { return (pairs + PERM_CHUNK - 1) / PERM_CHUNK; }
+
+// Instrumentation (moe_profile_start / moe_profile_stop): while recording, each
+// launch is bracketed by two events on its stream.  No-ops otherwise.
+void prof_begin(hipStream_t st);
+void prof_end(int tag, hipStream_t st);
+struct ProfScope {
+  int tag;
+  hipStream_t st;
+  ProfScope(int t, hipStream_t s) : tag(t), st(s) { prof_begin(s); }
+  ~ProfScope() { prof_end(tag, st); }
+};
+
+hipError_t launch_route(const moe_config_t& c, const void* x, const float* gate_w, const float* bias,
+                        int32_t* topk_idx, float* topk_w, float* logits_ws, hipStream_t st);
+
+hipError_t launch_permute(const moe_config_t& c, const int32_t* topk_idx, const void* x, int32_t* offsets,
+                          int32_t* sorted_pair, int32_t* pair_pos, void* x_perm, void* x_perm_scale,
+                          int32_t* hist_ws, hipStream_t st);
+
+// Scratch of the grouped FFN: tile list + SwiGLU output h (+ its scales).
+struct FfnScratch {
+  int32_t* tiles;        // [2 * max_tiles + 1]
+  void* h;               // [T*k][I] activation format
+  void* h_scale;         // fp32 [T*k][I/128] or E8M0 [T*k][I/32]
+};
+
+int ffn_row_tile(const moe_config_t& c);     // rows per tile (BM) of the routed grouped GEMM
+int ffn_max_tiles(const moe_config_t& c);     // upper bound of sum_e ceil(M_e / BM)
+
+hipError_t launch_grouped_ffn(const moe_config_t& c, const int32_t* offsets, const void* x_perm,
+                              const void* x_perm_scale, const moe_weights_t& w, void* y_perm,
+                              const FfnScratch& s, hipStream_t st);
+
+hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32_t* pair_pos, const float* topk_w,
+                          const void* x, const moe_weights_t* shared, void* out, void* h_shared, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,382 @@
+// C ABI of the MoE-layer forward library: argument checks, workspace carving and
+// the launch sequence of each entry point (declared and documented in include/moe.h).
+#include <algorithm>
+#include <vector>
+
+#include "gemm_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+hipError_t launch_bf16_swiglu(int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
+hipError_t launch_bf16_down(int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
+hipError_t launch_bf16_down_combine(int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
+hipError_t launch_lowp_swiglu(int recipe, int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
+hipError_t launch_lowp_down(int recipe, int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
+hipError_t launch_f32(int mode, int m_tiles, const GemmArgs& g, hipStream_t st);
+hipError_t launch_combine_only(const moe_config_t& c, const void* y_perm, const int32_t* pair_pos,
+                               const float* topk_w, void* out, hipStream_t st);
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int BM, int32_t* tiles, hipStream_t st);
+
+namespace {
+
+bool valid_config(const moe_config_t* c) {
+  if (!c) return false;
+  if (c->num_tokens < 0 || c->hidden <= 0 || c->intermediate <= 0 || c->num_experts <= 0) return false;
+  if (c->num_experts > 1024 || c->top_k < 1 || c->top_k > 16 || c->top_k > c->num_experts) return false;
+  if (c->num_shared < 0 || (c->num_shared > 0 && c->shared_intermediate <= 0)) return false;
+  if (c->n_group < 1 || c->n_group > 64 || c->num_experts % c->n_group != 0) return false;
+  if (c->topk_group < 1 || c->topk_group > c->n_group) return false;
+  if (c->n_group > 1 && c->num_experts / c->n_group < 2) return false;
+  if (int64_t(c->topk_group) * (c->num_experts / c->n_group) < c->top_k) return false;
+  if (c->score_func != MOE_SCORE_SIGMOID && c->score_func != MOE_SCORE_SQRTSOFTPLUS) return false;
+  if (c->recipe < MOE_RECIPE_F32 || c->recipe > MOE_RECIPE_MXFP4) return false;
+  if (!(c->routed_scaling_factor == c->routed_scaling_factor)) return false;
+  if (int64_t(c->num_tokens) * c->top_k > (int64_t(1) << 30)) return false;
+  return true;
+}
+
+bool supported_shape(const moe_config_t* c) {
+  const int q = (c->recipe == MOE_RECIPE_F32) ? 32 : 128;
+  if (c->hidden % q || c->intermediate % q) return false;
+  if (c->num_shared > 0 && c->shared_intermediate % q) return false;
+  return true;
+}
+
+size_t act_bytes(const moe_config_t& c) { return c.recipe == MOE_RECIPE_F32 ? 4 : 2; }     // x, y, out
+size_t routed_act_bytes(const moe_config_t& c) {                                             // x_perm, h
+  return c.recipe == MOE_RECIPE_F32 ? 4 : (c.recipe == MOE_RECIPE_BF16 ? 2 : 1);
+}
+size_t act_scale_bytes(const moe_config_t& c, int64_t rows, int64_t cols) {
+  if (c.recipe == MOE_RECIPE_FP8_B128) return size_t(rows * (cols / 128) * 4);
+  if (c.recipe == MOE_RECIPE_MXFP4) return size_t(rows * (cols / 32));
+  return 0;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Scratch layout; the same for every entry point so one size serves all of them.
+struct Layout {
+  size_t logits, hist, tiles, h, h_scale, h_shared, idx, w, offsets, sorted, pos, x_perm, x_perm_scale, y_perm, total;
+};
+
+Layout layout(const moe_config_t& c) {
+  Layout L{};
+  const int64_t T = c.num_tokens, E = c.num_experts, H = c.hidden, I = c.intermediate, P = T * c.top_k;
+  const int64_t SI = int64_t(c.num_shared) * c.shared_intermediate;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += align256(std::max<size_t>(bytes, 1)); return at; };
+  L.logits = take(size_t(T * E * 4));
+  L.hist = take(size_t(int64_t(perm_blocks(int(P))) * E * 4));
+  L.tiles = take(size_t((2 * int64_t(ffn_max_tiles(c)) + 1) * 4));
+  L.h = take(size_t(P * I) * routed_act_bytes(c));
+  L.h_scale = take(act_scale_bytes(c, P, I));
+  L.h_shared = take(size_t(T * SI) * act_bytes(c));
+  L.idx = take(size_t(P * 4));
+  L.w = take(size_t(P * 4));
+  L.offsets = take(size_t((E + 1) * 4));
+  L.sorted = take(size_t(P * 4));
+  L.pos = take(size_t(P * 4));
+  L.x_perm = take(size_t(P * H) * routed_act_bytes(c));
+  L.x_perm_scale = take(act_scale_bytes(c, P, H));
+  L.y_perm = take(size_t(P * H) * act_bytes(c));
+  L.total = o;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+int shared_ms(int T) { return T >= 96 ? 4 : (T >= 48 ? 2 : 1); }
+
+moe_status_t check_common(const moe_config_t* c, void* ws, size_t ws_bytes) {
+  if (!valid_config(c)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!supported_shape(c)) return MOE_ERR_UNSUPPORTED;
+  if (c->num_tokens == 0) return MOE_OK;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return MOE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < layout(*c).total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return MOE_OK;
+}
+
+bool quantised(const moe_config_t& c) { return c.recipe == MOE_RECIPE_FP8_B128 || c.recipe == MOE_RECIPE_MXFP4; }
+
+bool weights_ok(const moe_config_t& c, const moe_weights_t* w) {
+  if (!w || !w->w13 || !w->w2) return false;
+  if (quantised(c) && (!w->w13_scale || !w->w2_scale)) return false;
+  return true;
+}
+
+moe_status_t to_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+}  // namespace
+
+int ffn_row_tile(const moe_config_t& c) {
+  if (c.recipe == MOE_RECIPE_F32) return 16;
+  const int64_t avg = (int64_t(c.num_tokens) * c.top_k) / std::max(1, c.num_experts);
+  if (avg <= 40) return 32;
+  if (avg <= 96) return 64;
+  return 128;
+}
+
+int ffn_max_tiles(const moe_config_t& c) {
+  const int BM = ffn_row_tile(c);
+  const int64_t P = int64_t(c.num_tokens) * c.top_k;
+  return int((P + BM - 1) / BM + c.num_experts);
+}
+
+hipError_t launch_grouped_ffn(const moe_config_t& c, const int32_t* offsets, const void* x_perm,
+                              const void* x_perm_scale, const moe_weights_t& w, void* y_perm,
+                              const FfnScratch& s, hipStream_t st) {
+  const int BM = ffn_row_tile(c), ms = BM / 32, mt = ffn_max_tiles(c);
+  hipError_t e;
+  {
+    ProfScope p(MOE_K_TILES, st);
+    e = launch_build_tiles(offsets, c.num_experts, BM, s.tiles, st);
+  }
+  if (e != hipSuccess) return e;
+  GemmArgs g{};
+  g.A = x_perm;
+  g.A_scale = x_perm_scale;
+  g.lda = c.hidden;
+  g.offsets = offsets;
+  g.tiles = s.tiles;
+  g.B = w.w13;
+  g.B_scale = w.w13_scale;
+  g.K = c.hidden;
+  g.N = c.intermediate;
+  g.nsplit = c.intermediate;
+  g.n_experts_split = 1;
+  g.out = s.h;
+  g.out_scale = s.h_scale;
+  g.ldo = c.intermediate;
+  {
+    ProfScope p(MOE_K_FFN_GATE_UP, st);
+    if (c.recipe == MOE_RECIPE_F32) e = launch_f32(EPI_SWIGLU, mt, g, st);
+    else if (c.recipe == MOE_RECIPE_BF16) e = launch_bf16_swiglu(ms, mt, g, st);
+    else e = launch_lowp_swiglu(c.recipe, ms, mt, g, st);
+  }
+  if (e != hipSuccess) return e;
+  GemmArgs d = g;
+  d.A = s.h;
+  d.A_scale = s.h_scale;
+  d.lda = c.intermediate;
+  d.B = w.w2;
+  d.B_scale = w.w2_scale;
+  d.K = c.intermediate;
+  d.N = c.hidden;
+  d.nsplit = c.intermediate;
+  d.out = y_perm;
+  d.out_scale = nullptr;
+  d.ldo = c.hidden;
+  ProfScope p(MOE_K_FFN_DOWN, st);
+  if (c.recipe == MOE_RECIPE_F32) return launch_f32(EPI_STORE, mt, d, st);
+  if (c.recipe == MOE_RECIPE_BF16) return launch_bf16_down(ms, mt, d, st);
+  return launch_lowp_down(c.recipe, ms, mt, d, st);
+}
+
+hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32_t* pair_pos, const float* topk_w,
+                          const void* x, const moe_weights_t* shared, void* out, void* h_shared, hipStream_t st) {
+  if (c.num_shared == 0) {
+    ProfScope p(MOE_K_COMBINE, st);
+    return launch_combine_only(c, y_perm, pair_pos, topk_w, out, st);
+  }
+  const int T = c.num_tokens, SI = c.num_shared * c.shared_intermediate;
+  const bool f32 = c.recipe == MOE_RECIPE_F32;
+  const int ms = shared_ms(T), BM = f32 ? 16 : ms * 32, mt = (T + BM - 1) / BM;
+  GemmArgs g{};
+  g.A = x;
+  g.lda = c.hidden;
+  g.dense_rows = T;
+  g.B = shared->w13;
+  g.K = c.hidden;
+  g.N = SI;
+  g.nsplit = c.shared_intermediate;
+  g.n_experts_split = c.num_shared;
+  g.out = h_shared;
+  g.ldo = SI;
+  hipError_t e;
+  {
+    ProfScope p(MOE_K_SHARED_GATE_UP, st);
+    e = f32 ? launch_f32(EPI_SWIGLU, mt, g, st) : launch_bf16_swiglu(ms, mt, g, st);
+  }
+  if (e != hipSuccess) return e;
+  GemmArgs d = g;
+  d.A = h_shared;
+  d.lda = SI;
+  d.B = shared->w2;
+  d.K = SI;
+  d.N = c.hidden;
+  d.out = out;
+  d.ldo = c.hidden;
+  d.y_perm = y_perm;
+  d.pair_pos = pair_pos;
+  d.topk_w = topk_w;
+  d.topk = c.top_k;
+  ProfScope p(MOE_K_SHARED_DOWN_COMBINE, st);
+  return f32 ? launch_f32(EPI_COMBINE, mt, d, st) : launch_bf16_down_combine(ms, mt, d, st);
+}
+
+// ---------------------------------------------------------------- instrumentation
+namespace {
+struct ProfState {
+  bool on = false;
+  int cap = 0, n = 0;
+  std::vector<hipEvent_t> ev;   // 2 per launch
+  std::vector<int> tag;
+};
+ProfState g_prof;
+}  // namespace
+
+void prof_begin(hipStream_t st) {
+  if (g_prof.on && g_prof.n < g_prof.cap) (void)hipEventRecord(g_prof.ev[2 * g_prof.n], st);
+}
+void prof_end(int tag, hipStream_t st) {
+  if (g_prof.on && g_prof.n < g_prof.cap) {
+    (void)hipEventRecord(g_prof.ev[2 * g_prof.n + 1], st);
+    g_prof.tag[g_prof.n++] = tag;
+  }
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_config_t* cfg) {
+  if (!valid_config(cfg) || !supported_shape(cfg)) return 0;
+  return layout(*cfg).total;
+}
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or recipe";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+moe_status_t moe_profile_start(int32_t max_launches) {
+  if (max_launches <= 0 || g_prof.on) return MOE_ERR_INVALID_ARGUMENT;
+  g_prof.ev.assign(2 * size_t(max_launches), nullptr);
+  g_prof.tag.assign(size_t(max_launches), 0);
+  for (auto& e : g_prof.ev)
+    if (hipEventCreate(&e) != hipSuccess) return MOE_ERR_LAUNCH;
+  g_prof.cap = max_launches;
+  g_prof.n = 0;
+  g_prof.on = true;
+  return MOE_OK;
+}
+
+moe_status_t moe_profile_stop(double* ms_out, int64_t* count_out, int32_t n_tags) {
+  if (!g_prof.on) return MOE_ERR_INVALID_ARGUMENT;
+  moe_status_t st = MOE_OK;
+  for (int t = 0; t < n_tags; ++t) {
+    if (ms_out) ms_out[t] = 0.0;
+    if (count_out) count_out[t] = 0;
+  }
+  for (int i = 0; i < g_prof.n; ++i) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess) {
+      st = MOE_ERR_LAUNCH;
+      continue;
+    }
+    const int t = g_prof.tag[i];
+    if (t < n_tags) {
+      if (ms_out) ms_out[t] += ms;
+      if (count_out) count_out[t] += 1;
+    }
+  }
+  for (auto e : g_prof.ev) (void)hipEventDestroy(e);
+  g_prof = ProfState{};
+  return st;
+}
+
+const char* moe_kernel_tag_name(int32_t tag) {
+  static const char* names[MOE_K_COUNT] = {"gate_logits", "router", "perm_hist", "perm_scan", "perm_scatter",
+                                           "gather", "tile_list", "ffn_gate_up", "ffn_down", "shared_gate_up",
+                                           "shared_down_combine", "combine"};
+  return (tag >= 0 && tag < MOE_K_COUNT) ? names[tag] : "unknown";
+}
+
+moe_status_t moe_route(const moe_config_t* cfg, const void* x, const float* gate_w, const float* bias,
+                       int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t s = check_common(cfg, ws, ws_bytes);
+  if (s != MOE_OK || cfg->num_tokens == 0) return s;
+  if (!x || !gate_w || !bias || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARGUMENT;
+  const Layout L = layout(*cfg);
+  return to_status(launch_route(*cfg, x, gate_w, bias, topk_idx, topk_w, at<float>(ws, L.logits),
+                                static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_permute(const moe_config_t* cfg, const int32_t* topk_idx, const void* x, int32_t* expert_offsets,
+                         int32_t* sorted_pair, int32_t* pair_pos, void* x_perm, void* x_perm_scale, void* ws,
+                         size_t ws_bytes, void* stream) {
+  moe_status_t s = check_common(cfg, ws, ws_bytes);
+  if (s != MOE_OK || cfg->num_tokens == 0) return s;
+  if (!topk_idx || !x || !expert_offsets || !sorted_pair || !pair_pos || !x_perm) return MOE_ERR_INVALID_ARGUMENT;
+  if (quantised(*cfg) && !x_perm_scale) return MOE_ERR_INVALID_ARGUMENT;
+  const Layout L = layout(*cfg);
+  return to_status(launch_permute(*cfg, topk_idx, x, expert_offsets, sorted_pair, pair_pos, x_perm, x_perm_scale,
+                                  at<int32_t>(ws, L.hist), static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_grouped_ffn(const moe_config_t* cfg, const int32_t* expert_offsets, const void* x_perm,
+                             const void* x_perm_scale, const moe_weights_t* experts, void* y_perm, void* ws,
+                             size_t ws_bytes, void* stream) {
+  moe_status_t s = check_common(cfg, ws, ws_bytes);
+  if (s != MOE_OK || cfg->num_tokens == 0) return s;
+  if (!expert_offsets || !x_perm || !y_perm || !weights_ok(*cfg, experts)) return MOE_ERR_INVALID_ARGUMENT;
+  if (quantised(*cfg) && !x_perm_scale) return MOE_ERR_INVALID_ARGUMENT;
+  const Layout L = layout(*cfg);
+  FfnScratch sc{at<int32_t>(ws, L.tiles), at<void>(ws, L.h), at<void>(ws, L.h_scale)};
+  return to_status(launch_grouped_ffn(*cfg, expert_offsets, x_perm, x_perm_scale, *experts, y_perm, sc,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_combine(const moe_config_t* cfg, const void* y_perm, const int32_t* pair_pos, const float* topk_w,
+                         const void* x, const moe_weights_t* shared, void* out, void* ws, size_t ws_bytes,
+                         void* stream) {
+  moe_status_t s = check_common(cfg, ws, ws_bytes);
+  if (s != MOE_OK || cfg->num_tokens == 0) return s;
+  if (!y_perm || !pair_pos || !topk_w || !out) return MOE_ERR_INVALID_ARGUMENT;
+  if (cfg->num_shared > 0 && (!x || !shared || !shared->w13 || !shared->w2)) return MOE_ERR_INVALID_ARGUMENT;
+  const Layout L = layout(*cfg);
+  return to_status(launch_combine(*cfg, y_perm, pair_pos, topk_w, x, shared, out, at<void>(ws, L.h_shared),
+                                  static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* gate_w, const float* bias,
+                         const moe_weights_t* experts, const moe_weights_t* shared, void* out, int32_t* topk_idx_out,
+                         float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t s = check_common(cfg, ws, ws_bytes);
+  if (s != MOE_OK || cfg->num_tokens == 0) return s;
+  if (!x || !gate_w || !bias || !out || !weights_ok(*cfg, experts)) return MOE_ERR_INVALID_ARGUMENT;
+  if (cfg->num_shared > 0 && (!shared || !shared->w13 || !shared->w2)) return MOE_ERR_INVALID_ARGUMENT;
+  const moe_config_t& c = *cfg;
+  const Layout L = layout(c);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.idx);
+  float* w = topk_w_out ? topk_w_out : at<float>(ws, L.w);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* pos = at<int32_t>(ws, L.pos);
+  void* x_perm = at<void>(ws, L.x_perm);
+  void* x_perm_scale = quantised(c) ? at<void>(ws, L.x_perm_scale) : nullptr;
+  void* y_perm = at<void>(ws, L.y_perm);
+  hipError_t e = launch_route(c, x, gate_w, bias, idx, w, at<float>(ws, L.logits), st);
+  if (e == hipSuccess)
+    e = launch_permute(c, idx, x, offsets, at<int32_t>(ws, L.sorted), pos, x_perm, x_perm_scale,
+                       at<int32_t>(ws, L.hist), st);
+  if (e == hipSuccess) {
+    FfnScratch sc{at<int32_t>(ws, L.tiles), at<void>(ws, L.h), at<void>(ws, L.h_scale)};
+    e = launch_grouped_ffn(c, offsets, x_perm, x_perm_scale, *experts, y_perm, sc, st);
+  }
+  if (e == hipSuccess) e = launch_combine(c, y_perm, pos, w, x, shared, out, at<void>(ws, L.h_shared), st);
+  return to_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+"""The C-ABI library: it loads, exports every symbol include/moe.h declares, and
+rejects bad arguments on the host before touching the GPU.  CPU only."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_amd as M
+from workloads import configs as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(M.EXPORTS)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = M.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_config_struct_matches_header_layout():
+    # 12 int32 + 1 float, no padding
+    assert ctypes.sizeof(M.MoeConfig) == 13 * 4
+    assert ctypes.sizeof(M.MoeWeights) == 4 * ctypes.sizeof(ctypes.c_void_p)
+
+
+def test_status_strings():
+    lib = M.load()
+    assert lib.moe_status_string(0) == b"ok"
+    assert b"workspace" in lib.moe_status_string(3)
+
+
+@pytest.mark.parametrize("cfg", C.FULL_CONFIGS + C.MINI_CONFIGS, ids=lambda c: c.name)
+def test_workspace_sizes_are_positive_for_every_workload(cfg):
+    n = M.moe_workspace_bytes(M.make_config(cfg))
+    P, H = cfg.pairs, cfg.hidden
+    assert n >= P * H  # at least the permuted activations
+    assert n < 8 << 30
+
+
+BAD = [
+    dict(n_group=3),                       # E % n_group != 0 for E=16
+    dict(n_group=4, topk_group=5),         # topk_group > n_group
+    dict(n_group=16, topk_group=1),        # one expert per group
+    dict(n_group=4, topk_group=1, top_k=5),  # kept experts < k
+    dict(top_k=17),
+    dict(top_k=0),
+    dict(num_experts=2000, top_k=4),
+    dict(score_func=7),
+    dict(recipe=9),
+]
+
+
+@pytest.mark.parametrize("bad", BAD, ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_invalid_configs_are_rejected_without_launch(bad):
+    cfg = M.make_config(C.TINY_F32.replace(**bad))
+    assert M.moe_workspace_bytes(cfg) == 0
+    lib = M.load()
+    st = lib.moe_route(ctypes.byref(cfg), None, None, None, None, None, None, 0, None)
+    assert st == 1  # MOE_ERR_INVALID_ARGUMENT
+
+
+def test_unsupported_shapes_report_unsupported():
+    cfg = M.make_config(C.DECODE_BF16.replace(hidden=7100))
+    assert M.moe_workspace_bytes(cfg) == 0
+    st = M.load().moe_forward(ctypes.byref(cfg), None, None, None, None, None, None, None, None, None, 0, None)
+    assert st == 2  # MOE_ERR_UNSUPPORTED
+
+
+def test_null_pointers_and_small_workspace_are_rejected():
+    lib = M.load()
+    cfg = M.make_config(C.TINY_F32)
+    ws = ctypes.c_void_p(1 << 20)          # never dereferenced: validation fails first
+    st = lib.moe_route(ctypes.byref(cfg), None, None, None, None, None, ws, M.moe_workspace_bytes(cfg), None)
+    assert st == 1
+    fake = ctypes.c_void_p(4096)
+    st = lib.moe_route(ctypes.byref(cfg), fake, fake, fake, fake, fake, ws, 16, None)
+    assert st == 3  # MOE_ERR_WORKSPACE_TOO_SMALL
+    misaligned = ctypes.c_void_p((1 << 20) + 8)
+    st = lib.moe_route(ctypes.byref(cfg), fake, fake, fake, fake, fake, misaligned, 1 << 40, None)
+    assert st == 1
+
+
+def test_zero_tokens_is_a_no_op():
+    lib = M.load()
+    cfg = M.make_config(C.TINY_F32.replace(num_tokens=0))
+    assert lib.moe_forward(ctypes.byref(cfg), None, None, None, None, None, None, None, None, None, 0, None) == 0
