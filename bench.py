@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--config", default="decode_bf16")
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a known-size reference for HBM counters)")
     return ap.parse_args()
 
 
@@ -138,6 +140,13 @@ def main():
     def step():
         M.moe_forward(mcfg, inp.x, inp.gate_w, inp.bias, ex, sh, b.out, b.topk_idx, b.topk_w, b.ws)
 
+    if args.copy_calibration_mib:
+        src = torch.ones(args.copy_calibration_mib << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)                  # one elementwise kernel: reads and writes N MiB
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

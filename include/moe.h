@@ -201,8 +201,8 @@ typedef enum {
   MOE_K_FFN_GATE_UP,           /* routed grouped GEMM gate/up + SwiGLU (+ requant)    */
   MOE_K_FFN_DOWN,              /* routed grouped GEMM down projection                 */
   MOE_K_SHARED_GATE_UP,        /* shared expert(s) gate/up + SwiGLU                   */
-  MOE_K_SHARED_DOWN_COMBINE,   /* shared down projection + weighted put-back sum      */
-  MOE_K_COMBINE,               /* put-back sum alone (layers without shared experts) */
+  MOE_K_SHARED_DOWN_COMBINE,   /* shared down projection (fp32 recipe: + put-back sum) */
+  MOE_K_COMBINE,               /* weighted put-back sum (+ shared-expert rows)        */
   MOE_K_COUNT
 } moe_kernel_tag_t;
 

@@ -1,8 +1,7 @@
 // Per-expert SwiGLU MLP of moe_infer (DeepSeek-V3 walk-through, pwwt.cn/news/5781524,
 // section 3.4: each expert runs gate/up/down + SiLU over its contiguous block),
 // as a grouped bf16 MFMA GEMM on gfx950, and the shared expert(s) of
-// DeepseekV3MoE.forward with the weighted put-back sum fused into the epilogue
-// of their down projection.
+// DeepseekV3MoE.forward (their down projection stores fp32 rows for the put-back sum).
 //
 // Tile: BM = 32*MS rows x (SwiGLU: 128 h columns | down: 256 output columns),
 // four wavefronts.  The rows (activations) are staged through LDS, shared by the
@@ -143,8 +142,7 @@ __global__ __launch_bounds__(256) void ffn_bf16_kernel(GemmArgs g) {
           H[size_t(ti.row0 + row) * g.ldo + col] = f32_to_bf16(silu_f32(gt) * up);
         }
       }
-  } else if (MODE == EPI_STORE) {
-    uint16_t* Y = static_cast<uint16_t*>(g.out);
+  } else {  // EPI_STORE: bf16 y rows, or fp32 rows (out_f32)
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
       const int col = n0 + wave * 64 + f * 32 + l32;
@@ -153,30 +151,12 @@ __global__ __launch_bounds__(256) void ffn_bf16_kernel(GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = i * 32 + acc_row(r, lane);
-          if (row < ti.rows) Y[size_t(ti.row0 + row) * g.ldo + col] = f32_to_bf16(acc[i][f][r]);
+          if (row >= ti.rows) continue;
+          const size_t o = size_t(ti.row0 + row) * g.ldo + col;
+          if (g.out_f32) static_cast<float*>(g.out)[o] = acc[i][f][r];
+          else static_cast<uint16_t*>(g.out)[o] = f32_to_bf16(acc[i][f][r]);
         }
     }
-  } else {  // EPI_COMBINE: rows are tokens; add the weighted routed rows
-    uint16_t* O = static_cast<uint16_t*>(g.out);
-    const uint16_t* Yp = static_cast<const uint16_t*>(g.y_perm);
-    const int k = g.topk;
-#pragma unroll
-    for (int i = 0; i < MS; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = i * 32 + acc_row(r, lane);
-        if (row >= ti.rows) continue;
-        const int t = ti.row0 + row;
-        float sum0 = acc[i][0][r], sum1 = acc[i][1][r];
-        for (int j = 0; j < k; ++j) {
-          const float w = g.topk_w[size_t(t) * k + j];
-          const size_t yrow = size_t(g.pair_pos[size_t(t) * k + j]) * g.ldo;
-          sum0 += w * bf16_to_f32(Yp[yrow + n0 + wave * 64 + l32]);
-          sum1 += w * bf16_to_f32(Yp[yrow + n0 + wave * 64 + 32 + l32]);
-        }
-        O[size_t(t) * g.ldo + n0 + wave * 64 + l32] = f32_to_bf16(sum0);
-        O[size_t(t) * g.ldo + n0 + wave * 64 + 32 + l32] = f32_to_bf16(sum1);
-      }
   }
 }
 
@@ -198,9 +178,6 @@ hipError_t launch_bf16_swiglu(int ms, int m_tiles, const GemmArgs& g, hipStream_
 }
 hipError_t launch_bf16_down(int ms, int m_tiles, const GemmArgs& g, hipStream_t st) {
   return launch_ms<EPI_STORE>(ms, dim3((g.N + 255) / 256, m_tiles), g, st);
-}
-hipError_t launch_bf16_down_combine(int ms, int m_tiles, const GemmArgs& g, hipStream_t st) {
-  return launch_ms<EPI_COMBINE>(ms, dim3((g.N + 255) / 256, m_tiles), g, st);
 }
 
 }  // namespace moe

@@ -1,5 +1,5 @@
 // Tile lists for the grouped GEMMs, the fp32 expert MLP (VALU), and the
-// stand-alone weighted put-back sum used when a layer has no shared expert.
+// weighted put-back sum of the routed rows (plus the shared-expert rows).
 // moe_infer per-expert MLP and put-back: DeepSeek-V3 walk-through
 // (pwwt.cn/news/5781524), section 3.4.
 #include "gemm_common.h"
@@ -83,34 +83,69 @@ hipError_t launch_f32(int mode, int m_tiles, const GemmArgs& g, hipStream_t st) 
 }
 
 // ---------------------------------------------------------------------------
-// out[t] = sum_j w[t][j] * y_perm[pair_pos[t*k+j]] (no shared expert).
+// Put back + weighted sum (+ shared experts):
+//   out[t] = sum_j w[t][j] * y_perm[pair_pos[t*k+j]] (+ sh[t]), fp32 accumulation.
+// One workgroup per token; each thread owns 8 consecutive channels (16-byte loads).
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void combine_only(const T* __restrict__ yp, const int32_t* __restrict__ pair_pos,
-                                                    const float* __restrict__ w, int k, int H, T* __restrict__ out) {
+__global__ __launch_bounds__(256) void combine_bf16(const uint16_t* __restrict__ yp, const int32_t* __restrict__ pair_pos,
+                                                    const float* __restrict__ w, const float* __restrict__ sh, int k,
+                                                    int H, uint16_t* __restrict__ out) {
+  __shared__ int32_t pos[16];
+  __shared__ float wt[16];
   const int t = blockIdx.x;
-  for (int n = threadIdx.x; n < H; n += 256) {
-    float acc = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const size_t row = size_t(pair_pos[size_t(t) * k + j]) * H;
-      float y;
-      if constexpr (sizeof(T) == 4) y = yp[row + n];
-      else y = bf16_to_f32(yp[row + n]);
-      acc += w[size_t(t) * k + j] * y;
+  if (threadIdx.x < k) {
+    pos[threadIdx.x] = pair_pos[size_t(t) * k + threadIdx.x];
+    wt[threadIdx.x] = w[size_t(t) * k + threadIdx.x];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < H / 8; c += 256) {
+    float acc[8];
+    if (sh) {
+      const float4 a = reinterpret_cast<const float4*>(sh + size_t(t) * H)[2 * c];
+      const float4 b = reinterpret_cast<const float4*>(sh + size_t(t) * H)[2 * c + 1];
+      acc[0] = a.x; acc[1] = a.y; acc[2] = a.z; acc[3] = a.w; acc[4] = b.x; acc[5] = b.y; acc[6] = b.z; acc[7] = b.w;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
     }
-    if constexpr (sizeof(T) == 4) out[size_t(t) * H + n] = acc;
-    else out[size_t(t) * H + n] = f32_to_bf16(acc);
+    for (int j = 0; j < k; ++j) {
+      const uint4 v = reinterpret_cast<const uint4*>(yp + size_t(pos[j]) * H)[c];
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+      const float wj = wt[j];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += wj * __uint_as_float(u[q] << 16);
+        acc[2 * q + 1] += wj * __uint_as_float(u[q] & 0xffff0000u);
+      }
+    }
+    uint4 o;
+    o.x = uint32_t(f32_to_bf16(acc[0])) | (uint32_t(f32_to_bf16(acc[1])) << 16);
+    o.y = uint32_t(f32_to_bf16(acc[2])) | (uint32_t(f32_to_bf16(acc[3])) << 16);
+    o.z = uint32_t(f32_to_bf16(acc[4])) | (uint32_t(f32_to_bf16(acc[5])) << 16);
+    o.w = uint32_t(f32_to_bf16(acc[6])) | (uint32_t(f32_to_bf16(acc[7])) << 16);
+    reinterpret_cast<uint4*>(out + size_t(t) * H)[c] = o;
   }
 }
 
-hipError_t launch_combine_only(const moe_config_t& c, const void* y_perm, const int32_t* pair_pos,
-                               const float* topk_w, void* out, hipStream_t st) {
+__global__ __launch_bounds__(256) void combine_f32(const float* __restrict__ yp, const int32_t* __restrict__ pair_pos,
+                                                   const float* __restrict__ w, int k, int H, float* __restrict__ out) {
+  const int t = blockIdx.x;
+  for (int n = threadIdx.x; n < H; n += 256) {
+    float acc = 0.0f;
+    for (int j = 0; j < k; ++j) acc += w[size_t(t) * k + j] * yp[size_t(pair_pos[size_t(t) * k + j]) * H + n];
+    out[size_t(t) * H + n] = acc;
+  }
+}
+
+// sh: fp32 shared-expert rows [T][H] or nullptr (bf16-output recipes only).
+hipError_t launch_combine_rows(const moe_config_t& c, const void* y_perm, const int32_t* pair_pos,
+                               const float* topk_w, const float* sh, void* out, hipStream_t st) {
   if (c.recipe == MOE_RECIPE_F32)
-    combine_only<float><<<c.num_tokens, 256, 0, st>>>(static_cast<const float*>(y_perm), pair_pos, topk_w, c.top_k,
-                                                      c.hidden, static_cast<float*>(out));
+    combine_f32<<<c.num_tokens, 256, 0, st>>>(static_cast<const float*>(y_perm), pair_pos, topk_w, c.top_k,
+                                              c.hidden, static_cast<float*>(out));
   else
-    combine_only<uint16_t><<<c.num_tokens, 256, 0, st>>>(static_cast<const uint16_t*>(y_perm), pair_pos, topk_w,
-                                                         c.top_k, c.hidden, static_cast<uint16_t*>(out));
+    combine_bf16<<<c.num_tokens, 256, 0, st>>>(static_cast<const uint16_t*>(y_perm), pair_pos, topk_w, sh, c.top_k,
+                                               c.hidden, static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 

@@ -26,6 +26,7 @@ struct GemmArgs {
   void* out;                // [rows][N]
   void* out_scale;          // h scales for the quantised recipes
   int ldo;
+  int out_f32;              // down projection: store fp32 instead of bf16
   // combine epilogue
   const void* y_perm;
   const int32_t* pair_pos;

@@ -10,13 +10,14 @@ namespace moe {
 
 hipError_t launch_bf16_swiglu(int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
 hipError_t launch_bf16_down(int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
-hipError_t launch_bf16_down_combine(int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
 hipError_t launch_lowp_swiglu(int recipe, int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
 hipError_t launch_lowp_down(int recipe, int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
 hipError_t launch_f32(int mode, int m_tiles, const GemmArgs& g, hipStream_t st);
-hipError_t launch_combine_only(const moe_config_t& c, const void* y_perm, const int32_t* pair_pos,
-                               const float* topk_w, void* out, hipStream_t st);
+hipError_t launch_combine_rows(const moe_config_t& c, const void* y_perm, const int32_t* pair_pos,
+                               const float* topk_w, const float* sh, void* out, hipStream_t st);
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int BM, int32_t* tiles, hipStream_t st);
+hipError_t launch_lds_swiglu(bool fp8, int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
+hipError_t launch_lds_down(bool fp8, int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
 
 namespace {
 
@@ -57,7 +58,8 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Scratch layout; the same for every entry point so one size serves all of them.
 struct Layout {
-  size_t logits, hist, tiles, h, h_scale, h_shared, idx, w, offsets, sorted, pos, x_perm, x_perm_scale, y_perm, total;
+  size_t logits, hist, tiles, h, h_scale, h_shared, sh_out, idx, w, offsets, sorted, pos, x_perm, x_perm_scale, y_perm,
+      total;
 };
 
 Layout layout(const moe_config_t& c) {
@@ -72,6 +74,7 @@ Layout layout(const moe_config_t& c) {
   L.h = take(size_t(P * I) * routed_act_bytes(c));
   L.h_scale = take(act_scale_bytes(c, P, I));
   L.h_shared = take(size_t(T * SI) * act_bytes(c));
+  L.sh_out = take(c.recipe == MOE_RECIPE_F32 || SI == 0 ? 0 : size_t(T * H * 4));   // fp32 shared-expert rows
   L.idx = take(size_t(P * 4));
   L.w = take(size_t(P * 4));
   L.offsets = take(size_t((E + 1) * 4));
@@ -115,7 +118,14 @@ int ffn_row_tile(const moe_config_t& c) {
   const int64_t avg = (int64_t(c.num_tokens) * c.top_k) / std::max(1, c.num_experts);
   if (avg <= 40) return 32;
   if (avg <= 96) return 64;
-  return 128;
+  if (avg <= 192 || c.recipe != MOE_RECIPE_BF16) return 128;
+  return 256;
+}
+
+// The LDS-staged kernels serve bf16 and fp8 tiles of 64 rows and more; the
+// register-streaming kernels serve decode-sized tiles and the MXFP4 recipe.
+static bool use_lds_kernel(const moe_config_t& c, int BM) {
+  return (c.recipe == MOE_RECIPE_BF16 || c.recipe == MOE_RECIPE_FP8_B128) && BM >= 64;
 }
 
 int ffn_max_tiles(const moe_config_t& c) {
@@ -152,6 +162,7 @@ hipError_t launch_grouped_ffn(const moe_config_t& c, const int32_t* offsets, con
   {
     ProfScope p(MOE_K_FFN_GATE_UP, st);
     if (c.recipe == MOE_RECIPE_F32) e = launch_f32(EPI_SWIGLU, mt, g, st);
+    else if (use_lds_kernel(c, BM)) e = launch_lds_swiglu(c.recipe == MOE_RECIPE_FP8_B128, ms, mt, g, st);
     else if (c.recipe == MOE_RECIPE_BF16) e = launch_bf16_swiglu(ms, mt, g, st);
     else e = launch_lowp_swiglu(c.recipe, ms, mt, g, st);
   }
@@ -170,19 +181,23 @@ hipError_t launch_grouped_ffn(const moe_config_t& c, const int32_t* offsets, con
   d.ldo = c.hidden;
   ProfScope p(MOE_K_FFN_DOWN, st);
   if (c.recipe == MOE_RECIPE_F32) return launch_f32(EPI_STORE, mt, d, st);
+  if (use_lds_kernel(c, BM)) return launch_lds_down(c.recipe == MOE_RECIPE_FP8_B128, ms, mt, d, st);
   if (c.recipe == MOE_RECIPE_BF16) return launch_bf16_down(ms, mt, d, st);
   return launch_lowp_down(c.recipe, ms, mt, d, st);
 }
 
 hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32_t* pair_pos, const float* topk_w,
-                          const void* x, const moe_weights_t* shared, void* out, void* h_shared, hipStream_t st) {
+                          const void* x, const moe_weights_t* shared, void* out, void* h_shared, float* sh_out,
+                          hipStream_t st) {
   if (c.num_shared == 0) {
     ProfScope p(MOE_K_COMBINE, st);
-    return launch_combine_only(c, y_perm, pair_pos, topk_w, out, st);
+    return launch_combine_rows(c, y_perm, pair_pos, topk_w, nullptr, out, st);
   }
   const int T = c.num_tokens, SI = c.num_shared * c.shared_intermediate;
   const bool f32 = c.recipe == MOE_RECIPE_F32;
-  const int ms = shared_ms(T), BM = f32 ? 16 : ms * 32, mt = (T + BM - 1) / BM;
+  const bool lds = !f32 && T >= 128;                  // LDS-staged kernel for prefill-sized token counts
+  const int ms = lds ? (T >= 256 ? 8 : 4) : shared_ms(T);
+  const int BM = f32 ? 16 : ms * 32, mt = (T + BM - 1) / BM;
   GemmArgs g{};
   g.A = x;
   g.lda = c.hidden;
@@ -197,7 +212,8 @@ hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32
   hipError_t e;
   {
     ProfScope p(MOE_K_SHARED_GATE_UP, st);
-    e = f32 ? launch_f32(EPI_SWIGLU, mt, g, st) : launch_bf16_swiglu(ms, mt, g, st);
+    e = f32 ? launch_f32(EPI_SWIGLU, mt, g, st)
+            : (lds ? launch_lds_swiglu(false, ms, mt, g, st) : launch_bf16_swiglu(ms, mt, g, st));
   }
   if (e != hipSuccess) return e;
   GemmArgs d = g;
@@ -206,14 +222,25 @@ hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32
   d.B = shared->w2;
   d.K = SI;
   d.N = c.hidden;
-  d.out = out;
   d.ldo = c.hidden;
-  d.y_perm = y_perm;
-  d.pair_pos = pair_pos;
-  d.topk_w = topk_w;
-  d.topk = c.top_k;
-  ProfScope p(MOE_K_SHARED_DOWN_COMBINE, st);
-  return f32 ? launch_f32(EPI_COMBINE, mt, d, st) : launch_bf16_down_combine(ms, mt, d, st);
+  if (f32) {                                           // fp32: put-back sum fused into the down projection
+    d.out = out;
+    d.y_perm = y_perm;
+    d.pair_pos = pair_pos;
+    d.topk_w = topk_w;
+    d.topk = c.top_k;
+    ProfScope p(MOE_K_SHARED_DOWN_COMBINE, st);
+    return launch_f32(EPI_COMBINE, mt, d, st);
+  }
+  d.out = sh_out;                                      // fp32 shared rows, summed with the routed rows next
+  d.out_f32 = 1;
+  {
+    ProfScope p(MOE_K_SHARED_DOWN_COMBINE, st);
+    e = lds ? launch_lds_down(false, ms, mt, d, st) : launch_bf16_down(ms, mt, d, st);
+  }
+  if (e != hipSuccess) return e;
+  ProfScope p(MOE_K_COMBINE, st);
+  return launch_combine_rows(c, y_perm, pair_pos, topk_w, sh_out, out, st);
 }
 
 // ---------------------------------------------------------------- instrumentation
@@ -347,7 +374,7 @@ moe_status_t moe_combine(const moe_config_t* cfg, const void* y_perm, const int3
   if (cfg->num_shared > 0 && (!x || !shared || !shared->w13 || !shared->w2)) return MOE_ERR_INVALID_ARGUMENT;
   const Layout L = layout(*cfg);
   return to_status(launch_combine(*cfg, y_perm, pair_pos, topk_w, x, shared, out, at<void>(ws, L.h_shared),
-                                  static_cast<hipStream_t>(stream)));
+                                  at<float>(ws, L.sh_out), static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* gate_w, const float* bias,
@@ -375,7 +402,8 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* ga
     FfnScratch sc{at<int32_t>(ws, L.tiles), at<void>(ws, L.h), at<void>(ws, L.h_scale)};
     e = launch_grouped_ffn(c, offsets, x_perm, x_perm_scale, *experts, y_perm, sc, st);
   }
-  if (e == hipSuccess) e = launch_combine(c, y_perm, pos, w, x, shared, out, at<void>(ws, L.h_shared), st);
+  if (e == hipSuccess)
+    e = launch_combine(c, y_perm, pos, w, x, shared, out, at<void>(ws, L.h_shared), at<float>(ws, L.sh_out), st);
   return to_status(e);
 }
 

@@ -131,7 +131,20 @@ MINI_F32 = MoEConfig(
     recipe=RECIPE_F32, gate_std=1.0 / 16.0, bias_kind="uniform", bias_param=0.1,
     description="fp32 mini with ragged sizes")
 
-MINI_CONFIGS = [MINI_GROUPED_BF16, MINI_DECODE_BF16, MINI_MXFP4, MINI_FP8, MINI_F32]
+MINI_PREFILL_BF16 = MoEConfig(
+    name="mini_prefill_bf16", num_tokens=512, hidden=384, num_experts=8, top_k=4,
+    intermediate=256, num_shared=1, shared_intermediate=256, n_group=2, topk_group=2,
+    routed_scaling_factor=2.5, recipe=RECIPE_BF16, gate_std=1.0 / 16.0,
+    description="prefill-shaped bf16 mini: 256-row tiles, ragged experts, partial column tile")
+
+MINI_PREFILL_FP8 = MoEConfig(
+    name="mini_prefill_fp8", num_tokens=512, hidden=512, num_experts=8, top_k=2,
+    intermediate=256, num_shared=1, shared_intermediate=128,
+    score_func=SCORE_SQRTSOFTPLUS, routed_scaling_factor=2.5, recipe=RECIPE_FP8_B128,
+    gate_std=1.0 / 16.0, description="prefill-shaped fp8 mini: 128-row tiles")
+
+MINI_CONFIGS = [MINI_GROUPED_BF16, MINI_DECODE_BF16, MINI_MXFP4, MINI_FP8, MINI_F32, MINI_PREFILL_BF16,
+                MINI_PREFILL_FP8]
 
 BY_NAME = {c.name: c for c in FULL_CONFIGS + MINI_CONFIGS}
 
