@@ -63,6 +63,66 @@ __device__ __forceinline__ i32x8 cat(uint4 lo, uint4 hi) {
 
 }  // namespace
 
+// One stage (32 K of bf16) for the NJ row fragments of this wave that hold real
+// rows: every LDS operand read of the stage is issued before its MFMAs, with no
+// branch in between, so the reads overlap the matrix pipeline.
+template <int NJ, int MW>
+__device__ __forceinline__ void stage_bf16(f32x16 (&acc)[MW][4], const uint8_t* Ab, const uint8_t* Bb,
+                                           const int (&brow)[4], int wm, int l32, int half) {
+  bf16x8 bv[2][4], av[2][NJ];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int c = 2 * s + half;                        // k = 16s + 8h .. +8 of the stage
+#pragma unroll
+    for (int f = 0; f < 4; ++f) bv[s][f] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Bb + swz(brow[f], c)));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      av[s][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Ab + swz((wm + 2 * j) * 32 + l32, c)));
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) acc[j][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s][j], bv[s][f], acc[j][f], 0, 0, 0);
+}
+
+// One stage (64 K of fp8) with the 128x128-block scales: the MFMA runs with unit
+// scales and each fragment's partial sum is scaled by a_scale[row] * b_scale[block].
+template <int NJ, int MW>
+__device__ __forceinline__ void stage_fp8(f32x16 (&acc)[MW][4], const uint8_t* Ab, const uint8_t* Bb,
+                                          const float* Sab, const float (&sb)[4], const int (&brow)[4], int wm,
+                                          int l32, int half) {
+  i32x8 bv[4], av[NJ];
+  float ra[NJ][16];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+    bv[f] = cat(*reinterpret_cast<const uint4*>(Bb + swz(brow[f], 2 * half)),
+                *reinterpret_cast<const uint4*>(Bb + swz(brow[f], 2 * half + 1)));
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int i = wm + 2 * j;
+    av[j] = cat(*reinterpret_cast<const uint4*>(Ab + swz(i * 32 + l32, 2 * half)),
+                *reinterpret_cast<const uint4*>(Ab + swz(i * 32 + l32, 2 * half + 1)));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {                     // rows 8q + 4h + 0..3 of fragment i
+      const float4 v = *reinterpret_cast<const float4*>(Sab + i * 32 + 8 * q + 4 * half);
+      ra[j][4 * q] = v.x; ra[j][4 * q + 1] = v.y; ra[j][4 * q + 2] = v.z; ra[j][4 * q + 3] = v.w;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      f32x16 part;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part[r] = 0.0f;
+      part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[j], bv[f], part, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][f][r] += part[r] * (ra[j][r] * sb[f]);
+    }
+}
+
 template <int MS, int MODE, int KIND>
 __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(GemmArgs g) {
   constexpr int BM = MS * 32;
@@ -193,61 +253,26 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(GemmArgs g) {
       if (KIND == KIND_FP8) sa_reg[s] = load_sa(s * KS);
     }
   }
+  // row fragments of this wave that hold real rows (wave-uniform)
+  const int nj = min(MW, max(0, (act_ms - wm + 1) / 2));
   auto compute = [&](int kt, int buf) {
-      const uint8_t* Ab = As + buf * BM * ROWB;
-      const uint8_t* Bb = Bs + buf * NB * ROWB;
-      if (KIND == KIND_BF16) {
+    const uint8_t* Ab = As + buf * BM * ROWB;
+    const uint8_t* Bb = Bs + buf * NB * ROWB;
+    if (KIND == KIND_BF16) {
+      if (MW >= 4 && nj == 4) stage_bf16<(MW >= 4 ? 4 : 1), MW>(acc, Ab, Bb, brow, wm, l32, half);
+      else if (MW >= 3 && nj == 3) stage_bf16<(MW >= 3 ? 3 : 1), MW>(acc, Ab, Bb, brow, wm, l32, half);
+      else if (MW >= 2 && nj == 2) stage_bf16<(MW >= 2 ? 2 : 1), MW>(acc, Ab, Bb, brow, wm, l32, half);
+      else if (nj == 1) stage_bf16<1, MW>(acc, Ab, Bb, brow, wm, l32, half);
+    } else {
+      float sb[4];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int c = 2 * s + half;                    // k = 16s + 8h .. +8 of the stage
-          bf16x8 bv[4];
-#pragma unroll
-          for (int f = 0; f < 4; ++f) bv[f] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Bb + swz(brow[f], c)));
-#pragma unroll
-          for (int j = 0; j < MW; ++j) {
-            const int i = wm + 2 * j;
-            if (i < act_ms) {
-              const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Ab + swz(i * 32 + l32, c)));
-#pragma unroll
-              for (int f = 0; f < 4; ++f) acc[j][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv[f], acc[j][f], 0, 0, 0);
-            }
-          }
-        }
-      } else {
-        // fp8 x fp8, unit MFMA scales: lane half h takes bytes 32h .. +32 of the 64-byte row
-        const float* Sab = Sa + buf * BM;
-        i32x8 bv[4];
-        float sb[4];
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          bv[f] = cat(*reinterpret_cast<const uint4*>(Bb + swz(brow[f], 2 * half)),
-                      *reinterpret_cast<const uint4*>(Bb + swz(brow[f], 2 * half + 1)));
-          sb[f] = bscale_fp8(f, kt * KS);
-        }
-#pragma unroll
-        for (int j = 0; j < MW; ++j) {
-          const int i = wm + 2 * j;
-          if (i < act_ms) {
-            const i32x8 a = cat(*reinterpret_cast<const uint4*>(Ab + swz(i * 32 + l32, 2 * half)),
-                                *reinterpret_cast<const uint4*>(Ab + swz(i * 32 + l32, 2 * half + 1)));
-            float ra[16];                                  // rows 8q + 4h + 0..3 of fragment i
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float4 v = *reinterpret_cast<const float4*>(Sab + i * 32 + 8 * q + 4 * half);
-              ra[4 * q] = v.x; ra[4 * q + 1] = v.y; ra[4 * q + 2] = v.z; ra[4 * q + 3] = v.w;
-            }
-#pragma unroll
-            for (int f = 0; f < 4; ++f) {
-              f32x16 part;
-#pragma unroll
-              for (int r = 0; r < 16; ++r) part[r] = 0.0f;
-              part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bv[f], part, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-              for (int r = 0; r < 16; ++r) acc[j][f][r] += part[r] * (ra[r] * sb[f]);
-            }
-          }
-        }
-      }
+      for (int f = 0; f < 4; ++f) sb[f] = bscale_fp8(f, kt * KS);
+      const float* Sab = Sa + buf * BM;
+      if (MW >= 4 && nj == 4) stage_fp8<(MW >= 4 ? 4 : 1), MW>(acc, Ab, Bb, Sab, sb, brow, wm, l32, half);
+      else if (MW >= 3 && nj == 3) stage_fp8<(MW >= 3 ? 3 : 1), MW>(acc, Ab, Bb, Sab, sb, brow, wm, l32, half);
+      else if (MW >= 2 && nj == 2) stage_fp8<(MW >= 2 ? 2 : 1), MW>(acc, Ab, Bb, Sab, sb, brow, wm, l32, half);
+      else if (nj == 1) stage_fp8<1, MW>(acc, Ab, Bb, Sab, sb, brow, wm, l32, half);
+    }
   };
   for (int kt0 = 0; kt0 < KT; kt0 += NST) {
 #pragma unroll

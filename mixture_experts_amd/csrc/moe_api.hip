@@ -58,7 +58,7 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Scratch layout; the same for every entry point so one size serves all of them.
 struct Layout {
-  size_t logits, hist, tiles, h, h_scale, h_shared, sh_out, idx, w, offsets, sorted, pos, x_perm, x_perm_scale, y_perm,
+  size_t logits, gate_partial, hist, tiles, h, h_scale, h_shared, sh_out, idx, w, offsets, sorted, pos, x_perm, x_perm_scale, y_perm,
       total;
 };
 
@@ -69,6 +69,8 @@ Layout layout(const moe_config_t& c) {
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += align256(std::max<size_t>(bytes, 1)); return at; };
   L.logits = take(size_t(T * E * 4));
+  const int ks = gate_ksplit(c);
+  L.gate_partial = take(ks > 1 ? size_t(ks) * T * E * 8 : 0);
   L.hist = take(size_t(int64_t(perm_blocks(int(P))) * E * 4));
   L.tiles = take(size_t((2 * int64_t(ffn_max_tiles(c)) + 1) * 4));
   L.h = take(size_t(P * I) * routed_act_bytes(c));
@@ -337,7 +339,7 @@ moe_status_t moe_route(const moe_config_t* cfg, const void* x, const float* gate
   if (!x || !gate_w || !bias || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARGUMENT;
   const Layout L = layout(*cfg);
   return to_status(launch_route(*cfg, x, gate_w, bias, topk_idx, topk_w, at<float>(ws, L.logits),
-                                static_cast<hipStream_t>(stream)));
+                                at<double>(ws, L.gate_partial), static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_permute(const moe_config_t* cfg, const int32_t* topk_idx, const void* x, int32_t* expert_offsets,
@@ -394,7 +396,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* ga
   void* x_perm = at<void>(ws, L.x_perm);
   void* x_perm_scale = quantised(c) ? at<void>(ws, L.x_perm_scale) : nullptr;
   void* y_perm = at<void>(ws, L.y_perm);
-  hipError_t e = launch_route(c, x, gate_w, bias, idx, w, at<float>(ws, L.logits), st);
+  hipError_t e = launch_route(c, x, gate_w, bias, idx, w, at<float>(ws, L.logits), at<double>(ws, L.gate_partial), st);
   if (e == hipSuccess)
     e = launch_permute(c, idx, x, offsets, at<int32_t>(ws, L.sorted), pos, x_perm, x_perm_scale,
                        at<int32_t>(ws, L.hist), st);

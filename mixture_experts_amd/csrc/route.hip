@@ -29,9 +29,13 @@ __device__ __forceinline__ double load_x64<float>(const float* p) { return doubl
 template <>
 __device__ __forceinline__ double load_x64<uint16_t>(const uint16_t* p) { return double(bf16_to_f32(*p)); }
 
+// Split over K (blockIdx.z) when there are too few (token, expert) tiles to fill
+// the chip: each split writes fp64 partial sums, which the router adds in a fixed
+// order before the single rounding to fp32.
 template <typename XT>
 __global__ __launch_bounds__(256) void gate_logits_f64(const XT* __restrict__ x, const float* __restrict__ wg,
-                                                       float* __restrict__ logits, int T, int E, int H) {
+                                                       float* __restrict__ logits, double* __restrict__ partial,
+                                                       int T, int E, int H, int kchunk) {
   __shared__ double As[GT][GPAD];
   __shared__ double Bs[GE][GPAD];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -45,7 +49,8 @@ __global__ __launch_bounds__(256) void gate_logits_f64(const XT* __restrict__ x,
 
   // loader mapping: thread -> (row = tid / 4, 8 consecutive k at (tid % 4) * 8)
   const int lr = tid >> 2, lk = (tid & 3) * 8;
-  for (int k0 = 0; k0 < H; k0 += GK) {
+  const int kbeg = blockIdx.z * kchunk, kend = kbeg + kchunk;
+  for (int k0 = kbeg; k0 < kend; k0 += GK) {
     {
       const int t = t0 + lr;
       const bool ok = t < T;
@@ -83,7 +88,10 @@ __global__ __launch_bounds__(256) void gate_logits_f64(const XT* __restrict__ x,
       for (int r = 0; r < 4; ++r) {
         const int t = t0 + wr + i * 16 + r * 4 + (lane >> 4);
         const int e = e0 + wc + j * 16 + (lane & 15);
-        if (t < T && e < E) logits[size_t(t) * E + e] = float(acc[i][j][r]);
+        if (t < T && e < E) {
+          if (partial) partial[(size_t(blockIdx.z) * T + t) * E + e] = acc[i][j][r];
+          else logits[size_t(t) * E + e] = float(acc[i][j][r]);
+        }
       }
 }
 
@@ -106,7 +114,8 @@ constexpr int RT_WAVES = 4;
 constexpr int RT_MAXE = 1024;
 constexpr int RT_SLOTS = RT_MAXE / kWave;
 
-__global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ logits, const float* __restrict__ bias,
+__global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ logits, const double* __restrict__ partial,
+                                                     int nsplit, const float* __restrict__ bias,
                                                      int T, int E, int k, int n_group, int topk_group, int func,
                                                      int norm, float scale, int32_t* __restrict__ topk_idx,
                                                      float* __restrict__ topk_w) {
@@ -119,7 +128,15 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ l
   float* K = key_lds[wave];
   const float* lg = logits + size_t(valid ? t : 0) * E;
   for (int e = lane; e < E && valid; e += kWave) {
-    const float s = score_fp64(lg[e], func);
+    float logit;
+    if (partial) {                                      // K-split gate: fixed-order fp64 sum, one rounding
+      double z = 0.0;
+      for (int q = 0; q < nsplit; ++q) z += partial[(size_t(q) * T + t) * E + e];
+      logit = float(z);
+    } else {
+      logit = lg[e];
+    }
+    const float s = score_fp64(logit, func);
     float key = s + bias[e];
     key = (key == 0.0f) ? 0.0f : key;                  // -0 -> +0
     key = (key != key) ? -INFINITY : key;              // NaN ranks lowest
@@ -196,21 +213,34 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ l
 }
 
 // ---------------------------------------------------------------------------
+int gate_ksplit(const moe_config_t& c) {
+  const int tiles = ((c.num_experts + GE - 1) / GE) * ((c.num_tokens + GT - 1) / GT);
+  const int steps = c.hidden / GK;
+  int best = 1;
+  for (int d = 1; d <= steps && d <= 64; ++d)
+    if (steps % d == 0 && tiles * d <= 512) best = d;
+  return best;
+}
+
 hipError_t launch_route(const moe_config_t& c, const void* x, const float* gate_w, const float* bias,
-                        int32_t* topk_idx, float* topk_w, float* logits_ws, hipStream_t st) {
+                        int32_t* topk_idx, float* topk_w, float* logits_ws, double* partial_ws, hipStream_t st) {
   const int T = c.num_tokens, E = c.num_experts, H = c.hidden;
-  dim3 gg((E + GE - 1) / GE, (T + GT - 1) / GT);
+  const int ks = gate_ksplit(c);
+  double* partial = ks > 1 ? partial_ws : nullptr;
+  dim3 gg((E + GE - 1) / GE, (T + GT - 1) / GT, ks);
   {
     ProfScope p(MOE_K_GATE, st);
     if (c.recipe == MOE_RECIPE_F32)
-      gate_logits_f64<float><<<gg, 256, 0, st>>>(static_cast<const float*>(x), gate_w, logits_ws, T, E, H);
+      gate_logits_f64<float><<<gg, 256, 0, st>>>(static_cast<const float*>(x), gate_w, logits_ws, partial, T, E, H,
+                                                  H / ks);
     else
-      gate_logits_f64<uint16_t><<<gg, 256, 0, st>>>(static_cast<const uint16_t*>(x), gate_w, logits_ws, T, E, H);
+      gate_logits_f64<uint16_t><<<gg, 256, 0, st>>>(static_cast<const uint16_t*>(x), gate_w, logits_ws, partial, T,
+                                                     E, H, H / ks);
   }
   ProfScope p(MOE_K_ROUTER, st);
-  router_kernel<<<(T + RT_WAVES - 1) / RT_WAVES, 256, 0, st>>>(logits_ws, bias, T, E, c.top_k, c.n_group, c.topk_group,
-                                                              c.score_func, c.norm_topk_prob, c.routed_scaling_factor,
-                                                              topk_idx, topk_w);
+  router_kernel<<<(T + RT_WAVES - 1) / RT_WAVES, 256, 0, st>>>(logits_ws, partial, ks, bias, T, E, c.top_k, c.n_group,
+                                                              c.topk_group, c.score_func, c.norm_topk_prob,
+                                                              c.routed_scaling_factor, topk_idx, topk_w);
   return hipGetLastError();
 }
 
