@@ -29,13 +29,25 @@ namespace moe {
 
 namespace {
 
-constexpr int ROWB = 64;         // bytes of K per LDS row and stage
-constexpr int NST = 4;           // stages in the LDS ring
 constexpr int NB = 256;          // weight rows per tile
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__device__ __forceinline__ int swz(int r, int c) { return r * ROWB + ((c ^ (((r >> 1) ^ (r >> 2)) & 3)) << 4); }
+// Slot of logical 16-byte chunk c in LDS row r (rows of ROWB bytes).  For 64-byte rows
+// g(r) = ((r>>1) ^ (r>>2)) & 3, for 128-byte rows g(r) = (r ^ (r>>1)) & 7: in both
+// cases any 16 consecutive rows reading one chunk land on 16 distinct 16-byte slots
+// of a 256-byte bank window, and any 8 rows on 8 distinct slots of a 128-byte one.
+template <int ROWB>
+__device__ __forceinline__ int swz_slot(int r, int c) {
+  if (ROWB == 64) return c ^ (((r >> 1) ^ (r >> 2)) & 3);
+  return c ^ ((r ^ (r >> 1)) & 7);
+}
+template <int ROWB>
+__device__ __forceinline__ int swz(int r, int c) { return r * ROWB + (swz_slot<ROWB>(r, c) << 4); }
+
+__device__ __forceinline__ void async_copy4(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_wave_base, 4, 0, 0);
+}
 
 __device__ __forceinline__ void async_copy16(const void* g, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_wave_base, 16, 0, 0);
@@ -66,44 +78,52 @@ __device__ __forceinline__ i32x8 cat(uint4 lo, uint4 hi) {
 // One stage (32 K of bf16) for the NJ row fragments of this wave that hold real
 // rows: every LDS operand read of the stage is issued before its MFMAs, with no
 // branch in between, so the reads overlap the matrix pipeline.
-template <int NJ, int MW>
+template <int NJ, int MW, int ROWB>
 __device__ __forceinline__ void stage_bf16(f32x16 (&acc)[MW][4], const uint8_t* Ab, const uint8_t* Bb,
                                            const int (&brow)[4], int wm, int l32, int half) {
-  bf16x8 bv[2][4], av[2][NJ];
+  constexpr int NS = ROWB / 32;                        // 16-deep MFMA steps per stage
+  bf16x8 bv[NS][4], av[NS][NJ];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < NS; ++s) {
     const int c = 2 * s + half;                        // k = 16s + 8h .. +8 of the stage
 #pragma unroll
-    for (int f = 0; f < 4; ++f) bv[s][f] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Bb + swz(brow[f], c)));
+    for (int f = 0; f < 4; ++f) bv[s][f] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Bb + swz<ROWB>(brow[f], c)));
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
-      av[s][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Ab + swz((wm + 2 * j) * 32 + l32, c)));
+      av[s][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Ab + swz<ROWB>((wm + 2 * j) * 32 + l32, c)));
   }
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int f = 0; f < 4; ++f) acc[j][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s][j], bv[s][f], acc[j][f], 0, 0, 0);
 }
 
-// One stage (64 K of fp8) with the 128x128-block scales: the MFMA runs with unit
-// scales and each fragment's partial sum is scaled by a_scale[row] * b_scale[block].
-template <int NJ, int MW>
+// One stage (ROWB K of fp8) with the 128x128-block scales: the MFMA runs with unit
+// scales (lane half h takes bytes 64s + 32h .. +32 of the row at sub-step s) and
+// each fragment's partial sum is scaled by a_scale[row] * b_scale[block]; a stage
+// never straddles a 128-block.
+template <int NJ, int MW, int ROWB>
 __device__ __forceinline__ void stage_fp8(f32x16 (&acc)[MW][4], const uint8_t* Ab, const uint8_t* Bb,
                                           const float* Sab, const float (&sb)[4], const int (&brow)[4], int wm,
                                           int l32, int half) {
-  i32x8 bv[4], av[NJ];
+  constexpr int NS = ROWB / 64;
+  i32x8 bv[NS][4], av[NS][NJ];
   float ra[NJ][16];
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
-    bv[f] = cat(*reinterpret_cast<const uint4*>(Bb + swz(brow[f], 2 * half)),
-                *reinterpret_cast<const uint4*>(Bb + swz(brow[f], 2 * half + 1)));
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+      bv[s][f] = cat(*reinterpret_cast<const uint4*>(Bb + swz<ROWB>(brow[f], 4 * s + 2 * half)),
+                     *reinterpret_cast<const uint4*>(Bb + swz<ROWB>(brow[f], 4 * s + 2 * half + 1)));
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int i = wm + 2 * j;
-    av[j] = cat(*reinterpret_cast<const uint4*>(Ab + swz(i * 32 + l32, 2 * half)),
-                *reinterpret_cast<const uint4*>(Ab + swz(i * 32 + l32, 2 * half + 1)));
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      av[s][j] = cat(*reinterpret_cast<const uint4*>(Ab + swz<ROWB>(i * 32 + l32, 4 * s + 2 * half)),
+                     *reinterpret_cast<const uint4*>(Ab + swz<ROWB>(i * 32 + l32, 4 * s + 2 * half + 1)));
 #pragma unroll
     for (int q = 0; q < 4; ++q) {                     // rows 8q + 4h + 0..3 of fragment i
       const float4 v = *reinterpret_cast<const float4*>(Sab + i * 32 + 8 * q + 4 * half);
@@ -117,13 +137,19 @@ __device__ __forceinline__ void stage_fp8(f32x16 (&acc)[MW][4], const uint8_t* A
       f32x16 part;
 #pragma unroll
       for (int r = 0; r < 16; ++r) part[r] = 0.0f;
-      part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[j], bv[f], part, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[s][j], bv[s][f], part, 0, 0, 0, 127, 0, 127);
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][f][r] += part[r] * (ra[j][r] * sb[f]);
     }
 }
 
-template <int MS, int MODE, int KIND>
+// ROWB: bytes of K per LDS row and stage (64 or 128); NST: stages in the LDS ring;
+// PF: when > 0, every stage also touches (one 4-byte async copy into a dummy LDS
+// area per 128-byte line) the rows of the stage PF stages beyond the ring, so that
+// weight lines streaming from HBM are in L2 when their real copy is issued.
+template <int MS, int MODE, int KIND, int ROWB, int NST, int PF>
 __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(GemmArgs g) {
   constexpr int BM = MS * 32;
   constexpr int MW = MS / 2;                        // row fragments per wave
@@ -136,6 +162,7 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(GemmArgs g) {
   uint8_t* Bs = smem + NST * BM * ROWB;             // [NST][NB * ROWB]
   float* Sa = reinterpret_cast<float*>(Bs + NST * NB * ROWB);   // fp8: [NST][BM] row scales
   float* amax_lds = Sa + NST * BM;                               // fp8 epilogue: [2][BM]
+  uint8_t* pf_sink = reinterpret_cast<uint8_t*>(amax_lds + 2 * BM);  // [4][256] bytes, never read
 
   const int ncols = (MODE == EPI_SWIGLU) ? g.N / 128 : (g.N + NB - 1) / NB;
   const int ntiles_m = g.tiles ? g.tiles[0] : (g.dense_rows + BM - 1) / BM;
@@ -168,8 +195,8 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(GemmArgs g) {
   const uint8_t* a_src[A_INSTR];
 #pragma unroll
   for (int j = 0; j < A_INSTR; ++j) {
-    const int p = (wave * A_INSTR + j) * 64 + lane, r = p >> 2;
-    const int c = (p & 3) ^ (((r >> 1) ^ (r >> 2)) & 3);
+    const int p = (wave * A_INSTR + j) * 64 + lane, r = p / (ROWB / 16);
+    const int c = swz_slot<ROWB>(r, p % (ROWB / 16));
     const int row = ti.row0 + min(r, ti.rows - 1);
     a_src[j] = A + (size_t(row) * g.lda) * EB + c * 16;
   }
@@ -183,8 +210,8 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(GemmArgs g) {
   const uint8_t* b_src[B_INSTR];
 #pragma unroll
   for (int j = 0; j < B_INSTR; ++j) {
-    const int p = (wave * B_INSTR + j) * 64 + lane, r = p >> 2;
-    const int c = (p & 3) ^ (((r >> 1) ^ (r >> 2)) & 3);
+    const int p = (wave * B_INSTR + j) * 64 + lane, r = p / (ROWB / 16);
+    const int c = swz_slot<ROWB>(r, p % (ROWB / 16));
     size_t rowoff;
     if (MODE == EPI_SWIGLU) {
       const int wr = (r < 128) ? (n0 % ns + r) : (ns + n0 % ns + r - 128);
@@ -199,6 +226,27 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(GemmArgs g) {
     if (MODE == EPI_SWIGLU) return size_t(k0) * EB;
     return (size_t(k0 / ns) * g.N * ns + (k0 % ns)) * EB;
   };
+  // L2 prefetch: thread t touches tile rows t (and t + 256): A rows first, then weight rows
+  constexpr int PF_ROWS = (BM + NB + 255) / 256;
+  const uint8_t* pf_src[PF_ROWS];
+#pragma unroll
+  for (int q = 0; q < PF_ROWS; ++q) {
+    const int r = min(tid + 256 * q, BM + NB - 1);
+    if (r < BM) {
+      pf_src[q] = A + size_t(ti.row0 + min(r, ti.rows - 1)) * g.lda * EB;
+    } else {
+      const int br = r - BM;
+      size_t rowoff;
+      if (MODE == EPI_SWIGLU) {
+        const int wr = (br < 128) ? (n0 % ns + br) : (ns + n0 % ns + br - 128);
+        rowoff = (size_t(sub0) * 2 * ns + wr) * size_t(K);
+      } else {
+        const int n = min(n0 + br, g.N - 1);
+        rowoff = size_t(ti.e) * g.n_experts_split * g.N * ns + size_t(n) * ns;
+      }
+      pf_src[q] = B + rowoff * EB;
+    }
+  }
   auto issue = [&](int k0, int buf) {
 #pragma unroll
     for (int j = 0; j < A_INSTR; ++j)
@@ -206,6 +254,18 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(GemmArgs g) {
     const size_t ko = koff_bytes(k0);
 #pragma unroll
     for (int j = 0; j < B_INSTR; ++j) async_copy16(b_src[j] + ko, Bs + buf * NB * ROWB + (wave * B_INSTR + j) * 1024);
+    if (PF > 0) {
+      const int kp = k0 + PF * KS;
+      if (kp < K) {
+        const size_t ka = size_t(kp) * EB, kb = koff_bytes(kp);
+#pragma unroll
+        for (int q = 0; q < PF_ROWS; ++q)
+          async_copy4(pf_src[q] + (min(tid + 256 * q, BM + NB - 1) < BM ? ka : kb), pf_sink + wave * 256);
+      } else {
+#pragma unroll
+        for (int q = 0; q < PF_ROWS; ++q) async_copy4(pf_src[q], pf_sink + wave * 256);   // keeps the count per stage
+      }
+    }
   };
   // fp8 activation scale of row (tid % BM) for the 128-block holding k0.  Every
   // thread loads (rows clamped) so that all waves count the same loads in flight.
@@ -243,7 +303,7 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(GemmArgs g) {
       for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
 
   const int KT = K / KS;
-  constexpr int PER_STAGE = A_INSTR + B_INSTR + (KIND == KIND_FP8 ? 1 : 0);   // loads per stage per thread
+  constexpr int PER_STAGE = A_INSTR + B_INSTR + (KIND == KIND_FP8 ? 1 : 0) + (PF > 0 ? PF_ROWS : 0);
   float sa_reg[NST];
   // prologue: stages 0 .. NST-2 in flight
 #pragma unroll
@@ -259,19 +319,19 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(GemmArgs g) {
     const uint8_t* Ab = As + buf * BM * ROWB;
     const uint8_t* Bb = Bs + buf * NB * ROWB;
     if (KIND == KIND_BF16) {
-      if (MW >= 4 && nj == 4) stage_bf16<(MW >= 4 ? 4 : 1), MW>(acc, Ab, Bb, brow, wm, l32, half);
-      else if (MW >= 3 && nj == 3) stage_bf16<(MW >= 3 ? 3 : 1), MW>(acc, Ab, Bb, brow, wm, l32, half);
-      else if (MW >= 2 && nj == 2) stage_bf16<(MW >= 2 ? 2 : 1), MW>(acc, Ab, Bb, brow, wm, l32, half);
-      else if (nj == 1) stage_bf16<1, MW>(acc, Ab, Bb, brow, wm, l32, half);
+      if (MW >= 4 && nj == 4) stage_bf16<(MW >= 4 ? 4 : 1), MW, ROWB>(acc, Ab, Bb, brow, wm, l32, half);
+      else if (MW >= 3 && nj == 3) stage_bf16<(MW >= 3 ? 3 : 1), MW, ROWB>(acc, Ab, Bb, brow, wm, l32, half);
+      else if (MW >= 2 && nj == 2) stage_bf16<(MW >= 2 ? 2 : 1), MW, ROWB>(acc, Ab, Bb, brow, wm, l32, half);
+      else if (nj == 1) stage_bf16<1, MW, ROWB>(acc, Ab, Bb, brow, wm, l32, half);
     } else {
       float sb[4];
 #pragma unroll
       for (int f = 0; f < 4; ++f) sb[f] = bscale_fp8(f, kt * KS);
       const float* Sab = Sa + buf * BM;
-      if (MW >= 4 && nj == 4) stage_fp8<(MW >= 4 ? 4 : 1), MW>(acc, Ab, Bb, Sab, sb, brow, wm, l32, half);
-      else if (MW >= 3 && nj == 3) stage_fp8<(MW >= 3 ? 3 : 1), MW>(acc, Ab, Bb, Sab, sb, brow, wm, l32, half);
-      else if (MW >= 2 && nj == 2) stage_fp8<(MW >= 2 ? 2 : 1), MW>(acc, Ab, Bb, Sab, sb, brow, wm, l32, half);
-      else if (nj == 1) stage_fp8<1, MW>(acc, Ab, Bb, Sab, sb, brow, wm, l32, half);
+      if (MW >= 4 && nj == 4) stage_fp8<(MW >= 4 ? 4 : 1), MW, ROWB>(acc, Ab, Bb, Sab, sb, brow, wm, l32, half);
+      else if (MW >= 3 && nj == 3) stage_fp8<(MW >= 3 ? 3 : 1), MW, ROWB>(acc, Ab, Bb, Sab, sb, brow, wm, l32, half);
+      else if (MW >= 2 && nj == 2) stage_fp8<(MW >= 2 ? 2 : 1), MW, ROWB>(acc, Ab, Bb, Sab, sb, brow, wm, l32, half);
+      else if (nj == 1) stage_fp8<1, MW, ROWB>(acc, Ab, Bb, Sab, sb, brow, wm, l32, half);
     }
   };
   for (int kt0 = 0; kt0 < KT; kt0 += NST) {
@@ -281,8 +341,8 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(GemmArgs g) {
       if (kt >= KT) break;
       // wait until stage kt has landed (later stages may still be in flight)
       const int ahead = min(NST - 2, KT - 1 - kt);
-      if (ahead >= 2) wait_vmcnt<2 * PER_STAGE>();
-      else if (ahead == 1) wait_vmcnt<PER_STAGE>();
+      if (NST >= 4 && ahead >= 2) wait_vmcnt<(NST >= 4 ? 2 : 0) * PER_STAGE>();
+      else if (NST >= 3 && ahead >= 1) wait_vmcnt<PER_STAGE>();
       else wait_vmcnt<0>();
       if (KIND == KIND_FP8 && tid < BM) Sa[buf * BM + tid] = sa_reg[buf];
       __syncthreads();
@@ -376,26 +436,30 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(GemmArgs g) {
   }
 }
 
-size_t ffn_lds_smem(int ms, bool fp8) {
+template <int ROWB, int NST>
+size_t lds_smem_bytes(int ms, bool fp8) {
   const int BM = ms * 32;
-  return size_t(NST) * (BM + NB) * ROWB + (fp8 ? size_t(NST * BM + 2 * BM) * 4 : 0);
+  return size_t(NST) * (BM + NB) * ROWB + size_t(NST * BM + 2 * BM) * 4 + 4 * 256;
 }
 
-template <int MS, int MODE, int KIND>
-static void launch_one(dim3 grid, const GemmArgs& g, hipStream_t st) {
-  const size_t smem = ffn_lds_smem(MS, KIND == KIND_FP8);
-  auto kfn = ffn_lds_kernel<MS, MODE, KIND>;
+template <int MS, int MODE, int KIND, int ROWB, int NST, int PF>
+void launch_lds_variant(dim3 grid, const GemmArgs& g, hipStream_t st) {
+  const size_t smem = lds_smem_bytes<ROWB, NST>(MS, KIND == KIND_FP8);
+  auto kfn = ffn_lds_kernel<MS, MODE, KIND, ROWB, NST, PF>;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kfn), hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
   kfn<<<grid, 256, smem, st>>>(g);
 }
+
+// Production configuration of the LDS-staged kernels.
+constexpr int LDS_ROWB = 128, LDS_NST = 2, LDS_PF = 0;
 
 template <int MODE, int KIND>
 static hipError_t launch_lds_ms(int ms, int m_tiles, const GemmArgs& g, hipStream_t st) {
   const int ncols = (MODE == EPI_SWIGLU) ? g.N / 128 : (g.N + NB - 1) / NB;
   const dim3 grid(ncols, m_tiles);
-  if (ms <= 2) launch_one<2, MODE, KIND>(grid, g, st);
-  else if (ms <= 4 || KIND == KIND_FP8) launch_one<4, MODE, KIND>(grid, g, st);
-  else launch_one<8, MODE, KIND>(grid, g, st);
+  if (ms <= 2) launch_lds_variant<2, MODE, KIND, LDS_ROWB, LDS_NST, LDS_PF>(grid, g, st);
+  else if (ms <= 4 || KIND == KIND_FP8) launch_lds_variant<4, MODE, KIND, LDS_ROWB, LDS_NST, LDS_PF>(grid, g, st);
+  else launch_lds_variant<8, MODE, KIND, LDS_ROWB, LDS_NST, LDS_PF>(grid, g, st);
   return hipGetLastError();
 }
 

@@ -7,27 +7,42 @@
 
 namespace moe {
 
-// tiles = {count, e_0, m0_0, e_1, m0_1, ...}: every expert's rows cut into BM-row tiles.
-__global__ __launch_bounds__(1024) void build_tiles(const int32_t* __restrict__ offsets, int E, int BM,
-                                                    int32_t* __restrict__ tiles) {
-  __shared__ int32_t cnt[1024];
+// Two tile lists, {count, e_0, m0_0, e_1, m0_1, ...} each: experts with at least
+// `thresh` rows are cut into bm_large-row tiles (list L), the others into
+// bm_small-row tiles (list S).
+__global__ __launch_bounds__(1024) void build_tiles2(const int32_t* __restrict__ offsets, int E, int thresh,
+                                                     int bm_large, int bm_small, int32_t* __restrict__ tiles_l,
+                                                     int32_t* __restrict__ tiles_s) {
+  __shared__ int32_t cl[1024], cs[1024];
   const int e = threadIdx.x;
   const int m = (e < E) ? offsets[e + 1] - offsets[e] : 0;
-  const int n = (m + BM - 1) / BM;
-  cnt[e] = n;
+  const bool large = m >= thresh;
+  const int nl = large ? (m + bm_large - 1) / bm_large : 0;
+  const int nsm = large ? 0 : (m + bm_small - 1) / bm_small;
+  cl[e] = nl;
+  cs[e] = nsm;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
-    const int v = (e >= off) ? cnt[e - off] : 0;
+    const int vl = (e >= off) ? cl[e - off] : 0;
+    const int vs = (e >= off) ? cs[e - off] : 0;
     __syncthreads();
-    cnt[e] += v;
+    cl[e] += vl;
+    cs[e] += vs;
     __syncthreads();
   }
-  const int first = cnt[e] - n;
-  for (int q = 0; q < n; ++q) {
-    tiles[1 + 2 * (first + q)] = e;
-    tiles[2 + 2 * (first + q)] = q * BM;
+  const int fl = cl[e] - nl, fs = cs[e] - nsm;
+  for (int q = 0; q < nl; ++q) {
+    tiles_l[1 + 2 * (fl + q)] = e;
+    tiles_l[2 + 2 * (fl + q)] = q * bm_large;
   }
-  if (e == 1023) tiles[0] = cnt[1023];
+  for (int q = 0; q < nsm; ++q) {
+    tiles_s[1 + 2 * (fs + q)] = e;
+    tiles_s[2 + 2 * (fs + q)] = q * bm_small;
+  }
+  if (e == 1023) {
+    tiles_l[0] = cl[1023];
+    tiles_s[0] = cs[1023];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -149,8 +164,9 @@ hipError_t launch_combine_rows(const moe_config_t& c, const void* y_perm, const 
   return hipGetLastError();
 }
 
-hipError_t launch_build_tiles(const int32_t* offsets, int E, int BM, int32_t* tiles, hipStream_t st) {
-  build_tiles<<<1, 1024, 0, st>>>(offsets, E, BM, tiles);
+hipError_t launch_build_tiles2(const int32_t* offsets, int E, int thresh, int bm_large, int bm_small,
+                               int32_t* tiles_l, int32_t* tiles_s, hipStream_t st) {
+  build_tiles2<<<1, 1024, 0, st>>>(offsets, E, thresh, bm_large, bm_small, tiles_l, tiles_s);
   return hipGetLastError();
 }
 

@@ -30,15 +30,22 @@ hipError_t launch_permute(const moe_config_t& c, const int32_t* topk_idx, const 
                           int32_t* sorted_pair, int32_t* pair_pos, void* x_perm, void* x_perm_scale,
                           int32_t* hist_ws, hipStream_t st);
 
-// Scratch of the grouped FFN: tile list + SwiGLU output h (+ its scales).
+// Scratch of the grouped FFN: tile lists + SwiGLU output h (+ its scales).
 struct FfnScratch {
-  int32_t* tiles;        // [2 * max_tiles + 1]
+  int32_t* tiles_l;      // tiles of experts with many rows (LDS-staged kernel)
+  int32_t* tiles_s;      // tiles of experts with few rows (register-streaming kernel)
   void* h;               // [T*k][I] activation format
   void* h_scale;         // fp32 [T*k][I/128] or E8M0 [T*k][I/32]
 };
 
-int ffn_row_tile(const moe_config_t& c);     // rows per tile (BM) of the routed grouped GEMM
-int ffn_max_tiles(const moe_config_t& c);     // upper bound of sum_e ceil(M_e / BM)
+// How the routed experts' rows are cut into tiles and which kernel runs them.
+struct FfnPlan {
+  bool f32;              // fp32 recipe: VALU kernel, 16-row tiles (list S only)
+  int thresh;            // experts with >= thresh rows go to list L
+  int bm_l, bm_s;        // rows per tile of each list
+  int max_l, max_s;      // grid bounds of each list
+};
+FfnPlan ffn_plan(const moe_config_t& c);
 
 hipError_t launch_grouped_ffn(const moe_config_t& c, const int32_t* offsets, const void* x_perm,
                               const void* x_perm_scale, const moe_weights_t& w, void* y_perm,

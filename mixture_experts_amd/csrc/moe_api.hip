@@ -1,6 +1,7 @@
 // C ABI of the MoE-layer forward library: argument checks, workspace carving and
 // the launch sequence of each entry point (declared and documented in include/moe.h).
 #include <algorithm>
+#include <climits>
 #include <vector>
 
 #include "gemm_common.h"
@@ -8,14 +9,13 @@
 
 namespace moe {
 
-hipError_t launch_bf16_swiglu(int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
-hipError_t launch_bf16_down(int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
-hipError_t launch_lowp_swiglu(int recipe, int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
-hipError_t launch_lowp_down(int recipe, int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
+hipError_t launch_rs_swiglu(int recipe, int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
+hipError_t launch_rs_down(int recipe, int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
 hipError_t launch_f32(int mode, int m_tiles, const GemmArgs& g, hipStream_t st);
 hipError_t launch_combine_rows(const moe_config_t& c, const void* y_perm, const int32_t* pair_pos,
                                const float* topk_w, const float* sh, void* out, hipStream_t st);
-hipError_t launch_build_tiles(const int32_t* offsets, int E, int BM, int32_t* tiles, hipStream_t st);
+hipError_t launch_build_tiles2(const int32_t* offsets, int E, int thresh, int bm_large, int bm_small,
+                               int32_t* tiles_l, int32_t* tiles_s, hipStream_t st);
 hipError_t launch_lds_swiglu(bool fp8, int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
 hipError_t launch_lds_down(bool fp8, int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
 
@@ -58,7 +58,7 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Scratch layout; the same for every entry point so one size serves all of them.
 struct Layout {
-  size_t logits, gate_partial, hist, tiles, h, h_scale, h_shared, sh_out, idx, w, offsets, sorted, pos, x_perm, x_perm_scale, y_perm,
+  size_t logits, gate_partial, hist, tiles_l, tiles_s, h, h_scale, h_shared, sh_out, idx, w, offsets, sorted, pos, x_perm, x_perm_scale, y_perm,
       total;
 };
 
@@ -72,7 +72,9 @@ Layout layout(const moe_config_t& c) {
   const int ks = gate_ksplit(c);
   L.gate_partial = take(ks > 1 ? size_t(ks) * T * E * 8 : 0);
   L.hist = take(size_t(int64_t(perm_blocks(int(P))) * E * 4));
-  L.tiles = take(size_t((2 * int64_t(ffn_max_tiles(c)) + 1) * 4));
+  const FfnPlan fp = ffn_plan(c);
+  L.tiles_l = take(size_t((2 * int64_t(fp.max_l) + 1) * 4));
+  L.tiles_s = take(size_t((2 * int64_t(fp.max_s) + 1) * 4));
   L.h = take(size_t(P * I) * routed_act_bytes(c));
   L.h_scale = take(act_scale_bytes(c, P, I));
   L.h_shared = take(size_t(T * SI) * act_bytes(c));
@@ -92,7 +94,7 @@ Layout layout(const moe_config_t& c) {
 template <typename T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
 
-int shared_ms(int T) { return T >= 96 ? 4 : (T >= 48 ? 2 : 1); }
+int shared_ms(int T) { return T > 32 ? 2 : 1; }   // register-streaming tiles for small token counts
 
 moe_status_t check_common(const moe_config_t* c, void* ws, size_t ws_bytes) {
   if (!valid_config(c)) return MOE_ERR_INVALID_ARGUMENT;
@@ -115,43 +117,47 @@ moe_status_t to_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR
 
 }  // namespace
 
-int ffn_row_tile(const moe_config_t& c) {
-  if (c.recipe == MOE_RECIPE_F32) return 16;
-  const int64_t avg = (int64_t(c.num_tokens) * c.top_k) / std::max(1, c.num_experts);
-  if (avg <= 40) return 32;
-  if (avg <= 96) return 64;
-  if (avg <= 192 || c.recipe != MOE_RECIPE_BF16) return 128;
-  return 256;
-}
-
-// The LDS-staged kernels serve bf16 and fp8 tiles of 64 rows and more; the
-// register-streaming kernels serve decode-sized tiles and the MXFP4 recipe.
-static bool use_lds_kernel(const moe_config_t& c, int BM) {
-  return (c.recipe == MOE_RECIPE_BF16 || c.recipe == MOE_RECIPE_FP8_B128) && BM >= 64;
-}
-
-int ffn_max_tiles(const moe_config_t& c) {
-  const int BM = ffn_row_tile(c);
-  const int64_t P = int64_t(c.num_tokens) * c.top_k;
-  return int((P + BM - 1) / BM + c.num_experts);
+// Experts with at least 128 rows run on the LDS-staged kernel (bf16: 256-row
+// tiles, fp8: 128); experts with fewer rows, every decode-sized expert and the
+// MXFP4 recipe run on the register-streaming kernel with 32- or 64-row tiles.
+FfnPlan ffn_plan(const moe_config_t& c) {
+  FfnPlan p{};
+  const int64_t P = int64_t(c.num_tokens) * c.top_k, E = c.num_experts;
+  if (c.recipe == MOE_RECIPE_F32) {
+    p.f32 = true;
+    p.thresh = INT32_MAX;
+    p.bm_l = p.bm_s = 16;
+    p.max_l = 0;
+    p.max_s = int((P + 15) / 16 + E);
+    return p;
+  }
+  const int64_t avg = P / std::max<int64_t>(1, E);
+  p.bm_s = avg <= 40 ? 32 : 64;
+  p.thresh = (c.recipe == MOE_RECIPE_MXFP4) ? INT32_MAX : 128;
+  p.bm_l = (c.recipe == MOE_RECIPE_BF16) ? 256 : 128;
+  p.max_l = (p.thresh == INT32_MAX || P < p.thresh) ? 0 : int((P + p.bm_l - 1) / p.bm_l + std::min<int64_t>(E, P / p.thresh));
+  const int64_t small_bound = (p.thresh == INT32_MAX) ? (P + p.bm_s - 1) / p.bm_s + E
+                                                      : E * ((p.thresh + p.bm_s - 1) / p.bm_s);
+  p.max_s = int(std::min<int64_t>((P + p.bm_s - 1) / p.bm_s + E, small_bound));
+  return p;
 }
 
 hipError_t launch_grouped_ffn(const moe_config_t& c, const int32_t* offsets, const void* x_perm,
                               const void* x_perm_scale, const moe_weights_t& w, void* y_perm,
                               const FfnScratch& s, hipStream_t st) {
-  const int BM = ffn_row_tile(c), ms = BM / 32, mt = ffn_max_tiles(c);
+  const FfnPlan fp = ffn_plan(c);
   hipError_t e;
   {
     ProfScope p(MOE_K_TILES, st);
-    e = launch_build_tiles(offsets, c.num_experts, BM, s.tiles, st);
+    e = launch_build_tiles2(offsets, c.num_experts, fp.thresh, fp.bm_l, fp.bm_s, s.tiles_l, s.tiles_s, st);
   }
   if (e != hipSuccess) return e;
+  const bool fp8 = c.recipe == MOE_RECIPE_FP8_B128;
   GemmArgs g{};
   g.A = x_perm;
   g.A_scale = x_perm_scale;
   g.lda = c.hidden;
   g.offsets = offsets;
-  g.tiles = s.tiles;
   g.B = w.w13;
   g.B_scale = w.w13_scale;
   g.K = c.hidden;
@@ -163,10 +169,19 @@ hipError_t launch_grouped_ffn(const moe_config_t& c, const int32_t* offsets, con
   g.ldo = c.intermediate;
   {
     ProfScope p(MOE_K_FFN_GATE_UP, st);
-    if (c.recipe == MOE_RECIPE_F32) e = launch_f32(EPI_SWIGLU, mt, g, st);
-    else if (use_lds_kernel(c, BM)) e = launch_lds_swiglu(c.recipe == MOE_RECIPE_FP8_B128, ms, mt, g, st);
-    else if (c.recipe == MOE_RECIPE_BF16) e = launch_bf16_swiglu(ms, mt, g, st);
-    else e = launch_lowp_swiglu(c.recipe, ms, mt, g, st);
+    if (fp.f32) {
+      g.tiles = s.tiles_s;
+      e = launch_f32(EPI_SWIGLU, fp.max_s, g, st);
+    } else {
+      if (fp.max_l > 0) {
+        g.tiles = s.tiles_l;
+        e = launch_lds_swiglu(fp8, fp.bm_l / 32, fp.max_l, g, st);
+      }
+      if (e == hipSuccess) {
+        g.tiles = s.tiles_s;
+        e = launch_rs_swiglu(c.recipe, fp.bm_s / 32, fp.max_s, g, st);
+      }
+    }
   }
   if (e != hipSuccess) return e;
   GemmArgs d = g;
@@ -182,10 +197,17 @@ hipError_t launch_grouped_ffn(const moe_config_t& c, const int32_t* offsets, con
   d.out_scale = nullptr;
   d.ldo = c.hidden;
   ProfScope p(MOE_K_FFN_DOWN, st);
-  if (c.recipe == MOE_RECIPE_F32) return launch_f32(EPI_STORE, mt, d, st);
-  if (use_lds_kernel(c, BM)) return launch_lds_down(c.recipe == MOE_RECIPE_FP8_B128, ms, mt, d, st);
-  if (c.recipe == MOE_RECIPE_BF16) return launch_bf16_down(ms, mt, d, st);
-  return launch_lowp_down(c.recipe, ms, mt, d, st);
+  if (fp.f32) {
+    d.tiles = s.tiles_s;
+    return launch_f32(EPI_STORE, fp.max_s, d, st);
+  }
+  if (fp.max_l > 0) {
+    d.tiles = s.tiles_l;
+    e = launch_lds_down(fp8, fp.bm_l / 32, fp.max_l, d, st);
+    if (e != hipSuccess) return e;
+  }
+  d.tiles = s.tiles_s;
+  return launch_rs_down(c.recipe, fp.bm_s / 32, fp.max_s, d, st);
 }
 
 hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32_t* pair_pos, const float* topk_w,
@@ -215,7 +237,7 @@ hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32
   {
     ProfScope p(MOE_K_SHARED_GATE_UP, st);
     e = f32 ? launch_f32(EPI_SWIGLU, mt, g, st)
-            : (lds ? launch_lds_swiglu(false, ms, mt, g, st) : launch_bf16_swiglu(ms, mt, g, st));
+            : (lds ? launch_lds_swiglu(false, ms, mt, g, st) : launch_rs_swiglu(MOE_RECIPE_BF16, ms, mt, g, st));
   }
   if (e != hipSuccess) return e;
   GemmArgs d = g;
@@ -238,7 +260,7 @@ hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32
   d.out_f32 = 1;
   {
     ProfScope p(MOE_K_SHARED_DOWN_COMBINE, st);
-    e = lds ? launch_lds_down(false, ms, mt, d, st) : launch_bf16_down(ms, mt, d, st);
+    e = lds ? launch_lds_down(false, ms, mt, d, st) : launch_rs_down(MOE_RECIPE_BF16, ms, mt, d, st);
   }
   if (e != hipSuccess) return e;
   ProfScope p(MOE_K_COMBINE, st);
@@ -362,7 +384,7 @@ moe_status_t moe_grouped_ffn(const moe_config_t* cfg, const int32_t* expert_offs
   if (!expert_offsets || !x_perm || !y_perm || !weights_ok(*cfg, experts)) return MOE_ERR_INVALID_ARGUMENT;
   if (quantised(*cfg) && !x_perm_scale) return MOE_ERR_INVALID_ARGUMENT;
   const Layout L = layout(*cfg);
-  FfnScratch sc{at<int32_t>(ws, L.tiles), at<void>(ws, L.h), at<void>(ws, L.h_scale)};
+  FfnScratch sc{at<int32_t>(ws, L.tiles_l), at<int32_t>(ws, L.tiles_s), at<void>(ws, L.h), at<void>(ws, L.h_scale)};
   return to_status(launch_grouped_ffn(*cfg, expert_offsets, x_perm, x_perm_scale, *experts, y_perm, sc,
                                       static_cast<hipStream_t>(stream)));
 }
@@ -401,7 +423,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* ga
     e = launch_permute(c, idx, x, offsets, at<int32_t>(ws, L.sorted), pos, x_perm, x_perm_scale,
                        at<int32_t>(ws, L.hist), st);
   if (e == hipSuccess) {
-    FfnScratch sc{at<int32_t>(ws, L.tiles), at<void>(ws, L.h), at<void>(ws, L.h_scale)};
+    FfnScratch sc{at<int32_t>(ws, L.tiles_l), at<int32_t>(ws, L.tiles_s), at<void>(ws, L.h), at<void>(ws, L.h_scale)};
     e = launch_grouped_ffn(c, offsets, x_perm, x_perm_scale, *experts, y_perm, sc, st);
   }
   if (e == hipSuccess)
