@@ -3,20 +3,22 @@
 // pwwt.cn/news/5781524, section 3.4), bf16 and fp8 (128x128 block scales).
 //
 // Tile: up to 32*MS rows x 256 weight rows (SwiGLU: 128 gate_proj rows and the
-// matching 128 up_proj rows; down: 256 output columns), four wavefronts in a
-// 2 x 2 arrangement.  Wave (wm, wn) owns the 32-row MFMA fragments wm, wm+2,
-// wm+4, ... and four 32-column fragments, so a partial tile (the last rows of an
-// expert) skips the same share of fragments in every wave and costs time in
-// proportion to its rows.
+// matching 128 up_proj rows; down: 256 output columns) on a WM x WN grid of
+// wavefronts.  Wave (wm, wn) owns the 32-row MFMA fragments wm, wm+WM, wm+2WM,
+// ... and 8/WN of the eight 32-wide weight fragments (SwiGLU: 4/WN gate fragments
+// and the matching up fragments, so that SiLU(g)*u pairs sit in the same lane and
+// register).  A partial tile (the last rows of an expert) skips the same share of
+// row fragments in every wave and costs time in proportion to its rows.
 //
 // Both operands are staged through LDS with gfx950's direct global->LDS 16-byte
-// loads (global_load_lds_dwordx4) into a four-stage ring of 64-byte rows (32 bf16
-// or 64 fp8 of K per stage), three stages in flight while one is consumed.  The
-// 16-byte chunk c of LDS row r sits at slot c ^ g(r), g(r) = ((r>>1) ^ (r>>2)) & 3:
-// any 16 consecutive rows reading one chunk hit 16 distinct 16-byte slots of a
-// 256-byte bank window (and any 8 rows, 8 distinct slots of a 128-byte window).
-// The XOR is applied on the global side, so the LDS writes of one copy
-// instruction (64 lanes x 16 bytes) stay contiguous as the hardware requires.
+// loads (global_load_lds_dwordx4) into a ring of NST stages of ROWB-byte rows
+// (ROWB/2 bf16 or ROWB fp8 of K per stage).  The 16-byte chunk c of LDS row r sits
+// at slot c ^ g(r), with g(r) = ((r>>1) ^ (r>>2)) & 3 for 64-byte rows and
+// (r ^ (r>>1)) & 7 for 128-byte rows: any 16 consecutive rows reading one chunk hit
+// 16 distinct 16-byte slots of a 256-byte bank window (and any 8 rows, 8 distinct
+// slots of a 128-byte window).  The XOR is applied on the global side, so the LDS
+// writes of one copy instruction (64 lanes x 16 bytes) stay contiguous as the
+// hardware requires.  128-byte rows take whole cache lines per stage.
 //
 // Tiles are numbered (row tile, column tile), column tile fastest, and mapped so
 // that consecutive numbers run on the same XCD: column tiles sharing an
@@ -45,10 +47,6 @@ __device__ __forceinline__ int swz_slot(int r, int c) {
 template <int ROWB>
 __device__ __forceinline__ int swz(int r, int c) { return r * ROWB + (swz_slot<ROWB>(r, c) << 4); }
 
-__device__ __forceinline__ void async_copy4(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_wave_base, 4, 0, 0);
-}
-
 __device__ __forceinline__ void async_copy16(const void* g, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_wave_base, 16, 0, 0);
 }
@@ -75,94 +73,109 @@ __device__ __forceinline__ i32x8 cat(uint4 lo, uint4 hi) {
 
 }  // namespace
 
-// One stage (32 K of bf16) for the NJ row fragments of this wave that hold real
-// rows: every LDS operand read of the stage is issued before its MFMAs, with no
-// branch in between, so the reads overlap the matrix pipeline.
-template <int NJ, int MW, int ROWB>
-__device__ __forceinline__ void stage_bf16(f32x16 (&acc)[MW][4], const uint8_t* Ab, const uint8_t* Bb,
-                                           const int (&brow)[4], int wm, int l32, int half) {
+// Every LDS row a wave reads is 32*m + l32 for its lane's l32, so its swizzle key
+// is that of l32: a fragment's operand sits at a constant offset from the wave's
+// base plus one per-lane offset per chunk.  Row offset of weight fragment f within
+// a wave's share: SwiGLU (SPLIT = gate fragments per wave) interleaves the gate
+// half (rows 0..127) and the up half (rows 128..255).
+template <int SPLIT>
+__device__ constexpr int bfrag_row(int f) { return SPLIT > 0 ? (f < SPLIT ? 0 : 128) + (f % SPLIT) * 32 : f * 32; }
+
+// One stage (ROWB/2 K of bf16) for the NJ row fragments of this wave that hold
+// real rows: every LDS operand read of the stage is issued before its MFMAs, with
+// no branch in between, so the reads overlap the matrix pipeline.
+template <int NJ, int MW, int NF, int WM, int ROWB, int SPLIT>
+__device__ __forceinline__ void stage_bf16(f32x16 (&acc)[MW][NF], const uint8_t* Aw, const uint8_t* Bw, int l32,
+                                           int half) {
   constexpr int NS = ROWB / 32;                        // 16-deep MFMA steps per stage
-  bf16x8 bv[NS][4], av[NS][NJ];
+  bf16x8 bv[NS][NF], av[NS][NJ];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const int c = 2 * s + half;                        // k = 16s + 8h .. +8 of the stage
+    const int off = l32 * ROWB + (swz_slot<ROWB>(l32, 2 * s + half) << 4);   // k = 16s + 8h .. +8
 #pragma unroll
-    for (int f = 0; f < 4; ++f) bv[s][f] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Bb + swz<ROWB>(brow[f], c)));
+    for (int f = 0; f < NF; ++f)
+      bv[s][f] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Bw + bfrag_row<SPLIT>(f) * ROWB + off));
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
-      av[s][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Ab + swz<ROWB>((wm + 2 * j) * 32 + l32, c)));
+      av[s][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Aw + WM * 32 * ROWB * j + off));
   }
 #pragma unroll
   for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int f = 0; f < 4; ++f) acc[j][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s][j], bv[s][f], acc[j][f], 0, 0, 0);
+      for (int f = 0; f < NF; ++f) acc[j][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s][j], bv[s][f], acc[j][f], 0, 0, 0);
 }
 
 // One stage (ROWB K of fp8) with the 128x128-block scales: the MFMA runs with unit
 // scales (lane half h takes bytes 64s + 32h .. +32 of the row at sub-step s) and
 // each fragment's partial sum is scaled by a_scale[row] * b_scale[block]; a stage
-// never straddles a 128-block.
-template <int NJ, int MW, int ROWB>
-__device__ __forceinline__ void stage_fp8(f32x16 (&acc)[MW][4], const uint8_t* Ab, const uint8_t* Bb,
-                                          const float* Sab, const float (&sb)[4], const int (&brow)[4], int wm,
-                                          int l32, int half) {
+// never straddles a 128-block.  Sw: this wave's row scales (its fragment 0 first).
+template <int NJ, int MW, int NF, int WM, int ROWB, int SPLIT>
+__device__ __forceinline__ void stage_fp8(f32x16 (&acc)[MW][NF], const uint8_t* Aw, const uint8_t* Bw,
+                                          const float* Sw, const float (&sb)[NF], int l32, int half) {
   constexpr int NS = ROWB / 64;
-  i32x8 bv[NS][4], av[NS][NJ];
-  float ra[NJ][16];
+  int off[NS][2];
 #pragma unroll
   for (int s = 0; s < NS; ++s)
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
-      bv[s][f] = cat(*reinterpret_cast<const uint4*>(Bb + swz<ROWB>(brow[f], 4 * s + 2 * half)),
-                     *reinterpret_cast<const uint4*>(Bb + swz<ROWB>(brow[f], 4 * s + 2 * half + 1)));
+    for (int q = 0; q < 2; ++q) off[s][q] = l32 * ROWB + (swz_slot<ROWB>(l32, 4 * s + 2 * half + q) << 4);
+  i32x8 bv[NS][NF];
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const uint8_t* p = Bw + bfrag_row<SPLIT>(f) * ROWB;
+      bv[s][f] = cat(*reinterpret_cast<const uint4*>(p + off[s][0]), *reinterpret_cast<const uint4*>(p + off[s][1]));
+    }
+  // one row fragment at a time: its operands and row scales live only for its MFMAs
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int i = wm + 2 * j;
+    const uint8_t* p = Aw + WM * 32 * ROWB * j;
+    i32x8 av[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-      av[s][j] = cat(*reinterpret_cast<const uint4*>(Ab + swz<ROWB>(i * 32 + l32, 4 * s + 2 * half)),
-                     *reinterpret_cast<const uint4*>(Ab + swz<ROWB>(i * 32 + l32, 4 * s + 2 * half + 1)));
+      av[s] = cat(*reinterpret_cast<const uint4*>(p + off[s][0]), *reinterpret_cast<const uint4*>(p + off[s][1]));
+    float ra[16];                                     // rows 8q + 4h + 0..3 of the fragment
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {                     // rows 8q + 4h + 0..3 of fragment i
-      const float4 v = *reinterpret_cast<const float4*>(Sab + i * 32 + 8 * q + 4 * half);
-      ra[j][4 * q] = v.x; ra[j][4 * q + 1] = v.y; ra[j][4 * q + 2] = v.z; ra[j][4 * q + 3] = v.w;
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = *reinterpret_cast<const float4*>(Sw + WM * 32 * j + 8 * q + 4 * half);
+      ra[4 * q] = v.x; ra[4 * q + 1] = v.y; ra[4 * q + 2] = v.z; ra[4 * q + 3] = v.w;
     }
-  }
 #pragma unroll
-  for (int j = 0; j < NJ; ++j)
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
+    for (int f = 0; f < NF; ++f) {
       f32x16 part;
 #pragma unroll
       for (int r = 0; r < 16; ++r) part[r] = 0.0f;
 #pragma unroll
       for (int s = 0; s < NS; ++s)
-        part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[s][j], bv[s][f], part, 0, 0, 0, 127, 0, 127);
+        part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[s], bv[s][f], part, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[j][f][r] += part[r] * (ra[j][r] * sb[f]);
+      for (int r = 0; r < 16; ++r) acc[j][f][r] += part[r] * (ra[r] * sb[f]);
     }
+  }
 }
 
-// ROWB: bytes of K per LDS row and stage (64 or 128); NST: stages in the LDS ring;
-// PF: when > 0, every stage also touches (one 4-byte async copy into a dummy LDS
-// area per 128-byte line) the rows of the stage PF stages beyond the ring, so that
-// weight lines streaming from HBM are in L2 when their real copy is issued.
-template <int MS, int MODE, int KIND, int ROWB, int NST, int PF>
-__global__ __launch_bounds__(256, 1) void ffn_lds_kernel(GemmArgs g) {
+// MS: 32-row fragments per tile; WM x WN: wavefront grid; ROWB: bytes of K per
+// LDS row and stage (64 or 128); NST: stages in the LDS ring.
+template <int MS, int MODE, int KIND, int WM, int WN, int ROWB, int NST>
+__global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
+  constexpr int NW = WM * WN;                       // wavefronts
   constexpr int BM = MS * 32;
-  constexpr int MW = MS / 2;                        // row fragments per wave
-  constexpr int A_INSTR = BM * (ROWB / 16) / 64 / 4;   // async copies per wave per stage (A)
-  constexpr int B_INSTR = NB * (ROWB / 16) / 64 / 4;   // (B)
+  constexpr int MW = MS / WM;                       // row fragments per wave
+  constexpr int NF = 8 / WN;                        // weight fragments per wave
+  constexpr int NFG = NF / 2;                       // SwiGLU: gate (= up) fragments per wave
+  constexpr int A_INSTR = BM * (ROWB / 16) / 64 / NW;   // async copies per wave per stage (A)
+  constexpr int B_INSTR = NB * (ROWB / 16) / 64 / NW;   // (B)
+  static_assert(MW >= 1 && NFG >= 1 && A_INSTR >= 1 && B_INSTR >= 1, "tile shape");
+  static_assert(MS * 32 * (ROWB / 16) == A_INSTR * 64 * NW, "A copies cover the stage");
   constexpr int EB = (KIND == KIND_BF16) ? 2 : 1;   // bytes per element
   constexpr int KS = ROWB / EB;                     // K per stage
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   uint8_t* As = smem;                               // [NST][BM * ROWB]
   uint8_t* Bs = smem + NST * BM * ROWB;             // [NST][NB * ROWB]
   float* Sa = reinterpret_cast<float*>(Bs + NST * NB * ROWB);   // fp8: [NST][BM] row scales
-  float* amax_lds = Sa + NST * BM;                               // fp8 epilogue: [2][BM]
-  uint8_t* pf_sink = reinterpret_cast<uint8_t*>(amax_lds + 2 * BM);  // [4][256] bytes, never read
+  float* amax_lds = Sa + NST * BM;                               // fp8 epilogue: [WN][BM]
 
   const int ncols = (MODE == EPI_SWIGLU) ? g.N / 128 : (g.N + NB - 1) / NB;
   const int ntiles_m = g.tiles ? g.tiles[0] : (g.dense_rows + BM - 1) / BM;
@@ -183,15 +196,15 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(GemmArgs g) {
   }
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave % WM, wn = wave / WM;
   const int K = g.K, ns = g.nsplit;
   const uint8_t* A = static_cast<const uint8_t*>(g.A);
   const uint8_t* B = static_cast<const uint8_t*>(g.B);
   const int act_ms = (ti.rows + 31) >> 5;           // 32-row fragments holding real rows
 
   // ---- global sources of this thread's async copies: copy j of wave w fills LDS
-  // chunk positions p = (w*INSTR + j)*64 + lane -> row p/4, slot p%4, logical chunk
-  // slot ^ g(row)
+  // chunk positions p = (w*INSTR + j)*64 + lane -> row p / (ROWB/16), slot
+  // p % (ROWB/16), logical chunk slot ^ g(row)
   const uint8_t* a_src[A_INSTR];
 #pragma unroll
   for (int j = 0; j < A_INSTR; ++j) {
@@ -226,27 +239,6 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(GemmArgs g) {
     if (MODE == EPI_SWIGLU) return size_t(k0) * EB;
     return (size_t(k0 / ns) * g.N * ns + (k0 % ns)) * EB;
   };
-  // L2 prefetch: thread t touches tile rows t (and t + 256): A rows first, then weight rows
-  constexpr int PF_ROWS = (BM + NB + 255) / 256;
-  const uint8_t* pf_src[PF_ROWS];
-#pragma unroll
-  for (int q = 0; q < PF_ROWS; ++q) {
-    const int r = min(tid + 256 * q, BM + NB - 1);
-    if (r < BM) {
-      pf_src[q] = A + size_t(ti.row0 + min(r, ti.rows - 1)) * g.lda * EB;
-    } else {
-      const int br = r - BM;
-      size_t rowoff;
-      if (MODE == EPI_SWIGLU) {
-        const int wr = (br < 128) ? (n0 % ns + br) : (ns + n0 % ns + br - 128);
-        rowoff = (size_t(sub0) * 2 * ns + wr) * size_t(K);
-      } else {
-        const int n = min(n0 + br, g.N - 1);
-        rowoff = size_t(ti.e) * g.n_experts_split * g.N * ns + size_t(n) * ns;
-      }
-      pf_src[q] = B + rowoff * EB;
-    }
-  }
   auto issue = [&](int k0, int buf) {
 #pragma unroll
     for (int j = 0; j < A_INSTR; ++j)
@@ -254,18 +246,6 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(GemmArgs g) {
     const size_t ko = koff_bytes(k0);
 #pragma unroll
     for (int j = 0; j < B_INSTR; ++j) async_copy16(b_src[j] + ko, Bs + buf * NB * ROWB + (wave * B_INSTR + j) * 1024);
-    if (PF > 0) {
-      const int kp = k0 + PF * KS;
-      if (kp < K) {
-        const size_t ka = size_t(kp) * EB, kb = koff_bytes(kp);
-#pragma unroll
-        for (int q = 0; q < PF_ROWS; ++q)
-          async_copy4(pf_src[q] + (min(tid + 256 * q, BM + NB - 1) < BM ? ka : kb), pf_sink + wave * 256);
-      } else {
-#pragma unroll
-        for (int q = 0; q < PF_ROWS; ++q) async_copy4(pf_src[q], pf_sink + wave * 256);   // keeps the count per stage
-      }
-    }
   };
   // fp8 activation scale of row (tid % BM) for the 128-block holding k0.  Every
   // thread loads (rows clamped) so that all waves count the same loads in flight.
@@ -274,36 +254,35 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(GemmArgs g) {
     const int r = min(tid % BM, ti.rows - 1);
     return S[size_t(ti.row0 + r) * (K / 128) + k0 / 128];
   };
+  // Tile-relative weight column of each of this wave's fragments (SwiGLU: the h
+  // column block of the gate/up pair); the wave's first LDS weight row.
+  constexpr int SPLIT = (MODE == EPI_SWIGLU) ? NFG : 0;
+  int fcol[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) fcol[f] = (MODE == EPI_SWIGLU) ? (wn * NFG + f % NFG) * 32 : (wn * NF + f) * 32;
+  const int brow0 = (MODE == EPI_SWIGLU) ? wn * NFG * 32 : wn * NF * 32;
   // fp8 weight scale of this wave's fragment f at k0 (uniform across the wave)
   auto bscale_fp8 = [&](int f, int k0) -> float {
     const float* S = static_cast<const float*>(g.B_scale);
     if (MODE == EPI_SWIGLU) {
-      const int rb = ((f < 2) ? (n0 % ns) : ns + (n0 % ns)) / 128;
+      const int rb = ((f < NFG) ? (n0 % ns) : ns + (n0 % ns)) / 128;
       return S[(size_t(sub0) * (2 * ns / 128) + rb) * (K / 128) + k0 / 128];
     }
     const int sub = ti.e * g.n_experts_split + k0 / ns;
-    const int cb = min(n0 + wn * 128 + f * 32, g.N - 1) / 128;
+    const int cb = min(n0 + fcol[f], g.N - 1) / 128;
     return S[(size_t(sub) * (g.N / 128) + cb) * (ns / 128) + (k0 % ns) / 128];
   };
 
-  // LDS weight rows of this wave's four fragments
-  int brow[4];
-#pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    if (MODE == EPI_SWIGLU) brow[f] = (f < 2 ? 0 : 128) + wn * 64 + (f & 1) * 32 + l32;
-    else brow[f] = wn * 128 + f * 32 + l32;
-  }
-
-  f32x16 acc[MW][4];
+  f32x16 acc[MW][NF];
 #pragma unroll
   for (int i = 0; i < MW; ++i)
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+    for (int f = 0; f < NF; ++f)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
 
   const int KT = K / KS;
-  constexpr int PER_STAGE = A_INSTR + B_INSTR + (KIND == KIND_FP8 ? 1 : 0) + (PF > 0 ? PF_ROWS : 0);
+  constexpr int PER_STAGE = A_INSTR + B_INSTR + (KIND == KIND_FP8 ? 1 : 0);   // loads per thread per stage
   float sa_reg[NST];
   // prologue: stages 0 .. NST-2 in flight
 #pragma unroll
@@ -314,24 +293,24 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(GemmArgs g) {
     }
   }
   // row fragments of this wave that hold real rows (wave-uniform)
-  const int nj = min(MW, max(0, (act_ms - wm + 1) / 2));
+  const int nj = min(MW, max(0, (act_ms - wm + WM - 1) / WM));
   auto compute = [&](int kt, int buf) {
-    const uint8_t* Ab = As + buf * BM * ROWB;
-    const uint8_t* Bb = Bs + buf * NB * ROWB;
+    const uint8_t* Aw = As + buf * BM * ROWB + wm * 32 * ROWB;
+    const uint8_t* Bw = Bs + buf * NB * ROWB + brow0 * ROWB;
     if (KIND == KIND_BF16) {
-      if (MW >= 4 && nj == 4) stage_bf16<(MW >= 4 ? 4 : 1), MW, ROWB>(acc, Ab, Bb, brow, wm, l32, half);
-      else if (MW >= 3 && nj == 3) stage_bf16<(MW >= 3 ? 3 : 1), MW, ROWB>(acc, Ab, Bb, brow, wm, l32, half);
-      else if (MW >= 2 && nj == 2) stage_bf16<(MW >= 2 ? 2 : 1), MW, ROWB>(acc, Ab, Bb, brow, wm, l32, half);
-      else if (nj == 1) stage_bf16<1, MW, ROWB>(acc, Ab, Bb, brow, wm, l32, half);
+      if (MW >= 4 && nj == 4) stage_bf16<(MW >= 4 ? 4 : 1), MW, NF, WM, ROWB, SPLIT>(acc, Aw, Bw, l32, half);
+      else if (MW >= 3 && nj == 3) stage_bf16<(MW >= 3 ? 3 : 1), MW, NF, WM, ROWB, SPLIT>(acc, Aw, Bw, l32, half);
+      else if (MW >= 2 && nj == 2) stage_bf16<(MW >= 2 ? 2 : 1), MW, NF, WM, ROWB, SPLIT>(acc, Aw, Bw, l32, half);
+      else if (nj == 1) stage_bf16<1, MW, NF, WM, ROWB, SPLIT>(acc, Aw, Bw, l32, half);
     } else {
-      float sb[4];
+      float sb[NF];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) sb[f] = bscale_fp8(f, kt * KS);
-      const float* Sab = Sa + buf * BM;
-      if (MW >= 4 && nj == 4) stage_fp8<(MW >= 4 ? 4 : 1), MW, ROWB>(acc, Ab, Bb, Sab, sb, brow, wm, l32, half);
-      else if (MW >= 3 && nj == 3) stage_fp8<(MW >= 3 ? 3 : 1), MW, ROWB>(acc, Ab, Bb, Sab, sb, brow, wm, l32, half);
-      else if (MW >= 2 && nj == 2) stage_fp8<(MW >= 2 ? 2 : 1), MW, ROWB>(acc, Ab, Bb, Sab, sb, brow, wm, l32, half);
-      else if (nj == 1) stage_fp8<1, MW, ROWB>(acc, Ab, Bb, Sab, sb, brow, wm, l32, half);
+      for (int f = 0; f < NF; ++f) sb[f] = bscale_fp8(f, kt * KS);
+      const float* Sw = Sa + buf * BM + wm * 32;
+      if (MW >= 4 && nj == 4) stage_fp8<(MW >= 4 ? 4 : 1), MW, NF, WM, ROWB, SPLIT>(acc, Aw, Bw, Sw, sb, l32, half);
+      else if (MW >= 3 && nj == 3) stage_fp8<(MW >= 3 ? 3 : 1), MW, NF, WM, ROWB, SPLIT>(acc, Aw, Bw, Sw, sb, l32, half);
+      else if (MW >= 2 && nj == 2) stage_fp8<(MW >= 2 ? 2 : 1), MW, NF, WM, ROWB, SPLIT>(acc, Aw, Bw, Sw, sb, l32, half);
+      else if (nj == 1) stage_fp8<1, MW, NF, WM, ROWB, SPLIT>(acc, Aw, Bw, Sw, sb, l32, half);
     }
   };
   for (int kt0 = 0; kt0 < KT; kt0 += NST) {
@@ -362,34 +341,34 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(GemmArgs g) {
       uint16_t* Hh = static_cast<uint16_t*>(g.out);
 #pragma unroll
       for (int j = 0; j < MW; ++j) {
-        const int i = wm + 2 * j;
+        const int i = wm + WM * j;
         if (i >= act_ms) continue;
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const int col = n0 + wn * 64 + f * 32 + l32;
+        for (int f = 0; f < NFG; ++f) {
+          const int col = n0 + fcol[f] + l32;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int row = i * 32 + acc_row(r, lane);
             if (row < ti.rows)
-              Hh[size_t(ti.row0 + row) * g.ldo + col] = f32_to_bf16(silu_f32(acc[j][f][r]) * acc[j][f + 2][r]);
+              Hh[size_t(ti.row0 + row) * g.ldo + col] = f32_to_bf16(silu_f32(acc[j][f][r]) * acc[j][f + NFG][r]);
           }
         }
       }
     } else {
       // h re-quantised per (row, 128 columns): the tile's 128 h columns are one block,
-      // split over the two column waves (64 each)
+      // split over the WN column waves
       uint8_t* Hq = static_cast<uint8_t*>(g.out);
 #pragma unroll
       for (int j = 0; j < MW; ++j) {
-        const int i = wm + 2 * j;
+        const int i = wm + WM * j;
         const bool on = i < act_ms;
-        float hv[2][16];
+        float hv[NFG][16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float m = 0.0f;
 #pragma unroll
-          for (int f = 0; f < 2; ++f) {
-            hv[f][r] = silu_f32(acc[j][f][r]) * acc[j][f + 2][r];
+          for (int f = 0; f < NFG; ++f) {
+            hv[f][r] = silu_f32(acc[j][f][r]) * acc[j][f + NFG][r];
             m = fmaxf(m, fabsf(hv[f][r]));
           }
           m = max_over_lanes32(m);
@@ -400,12 +379,14 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(GemmArgs g) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int row = i * 32 + acc_row(r, lane);
-            const float amax = fmaxf(amax_lds[row], amax_lds[BM + row]);
+            float amax = amax_lds[row];
+#pragma unroll
+            for (int q = 1; q < WN; ++q) amax = fmaxf(amax, amax_lds[q * BM + row]);
             const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
             if (row < ti.rows) {
 #pragma unroll
-              for (int f = 0; f < 2; ++f)
-                Hq[size_t(ti.row0 + row) * g.ldo + n0 + wn * 64 + f * 32 + l32] = uint8_t(f32_to_e4m3(hv[f][r] / s));
+              for (int f = 0; f < NFG; ++f)
+                Hq[size_t(ti.row0 + row) * g.ldo + n0 + fcol[f] + l32] = uint8_t(f32_to_e4m3(hv[f][r] / s));
               if (wn == 0 && l32 == 0)
                 static_cast<float*>(g.out_scale)[size_t(ti.row0 + row) * (g.N / 128) + n0 / 128] = s;
             }
@@ -416,12 +397,12 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(GemmArgs g) {
     }
   } else {  // EPI_STORE: bf16 y rows, or fp32 rows (out_f32)
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int col = n0 + wn * 128 + f * 32 + l32;
-      if (n0 + wn * 128 + f * 32 >= g.N) continue;      // partial column tile (g.N % 128 == 0)
+    for (int f = 0; f < NF; ++f) {
+      const int col = n0 + fcol[f] + l32;
+      if (n0 + fcol[f] >= g.N) continue;               // partial column tile (g.N % 128 == 0)
 #pragma unroll
       for (int j = 0; j < MW; ++j) {
-        const int i = wm + 2 * j;
+        const int i = wm + WM * j;
         if (i >= act_ms) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -436,30 +417,36 @@ __global__ __launch_bounds__(256, 1) void ffn_lds_kernel(GemmArgs g) {
   }
 }
 
-template <int ROWB, int NST>
-size_t lds_smem_bytes(int ms, bool fp8) {
-  const int BM = ms * 32;
-  return size_t(NST) * (BM + NB) * ROWB + size_t(NST * BM + 2 * BM) * 4 + 4 * 256;
+template <int MS, int WN, int ROWB, int NST>
+constexpr size_t lds_smem_bytes() {
+  return size_t(NST) * (MS * 32 + NB) * ROWB + size_t(NST + WN) * MS * 32 * 4;
 }
 
-template <int MS, int MODE, int KIND, int ROWB, int NST, int PF>
+template <int MS, int MODE, int KIND, int WM, int WN, int ROWB, int NST>
 void launch_lds_variant(dim3 grid, const GemmArgs& g, hipStream_t st) {
-  const size_t smem = lds_smem_bytes<ROWB, NST>(MS, KIND == KIND_FP8);
-  auto kfn = ffn_lds_kernel<MS, MODE, KIND, ROWB, NST, PF>;
+  constexpr size_t smem = lds_smem_bytes<MS, WN, ROWB, NST>();
+  static_assert(smem <= 160 * 1024, "LDS budget");
+  auto kfn = ffn_lds_kernel<MS, MODE, KIND, WM, WN, ROWB, NST>;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kfn), hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
-  kfn<<<grid, 256, smem, st>>>(g);
+  kfn<<<grid, 64 * WM * WN, smem, st>>>(g);
 }
 
-// Production configuration of the LDS-staged kernels.
-constexpr int LDS_ROWB = 128, LDS_NST = 2, LDS_PF = 0;
-
+// Production configurations, 128-byte rows in a two-stage ring.  bf16: 2 x 2
+// wavefronts, up to 256-row tiles (the accumulators stay in the MFMA's own
+// registers).  fp8: 2 x 4 wavefronts (two per SIMD), so that 256-row tiles fit:
+// the block-scale FMAs keep the accumulators in ordinary VGPRs.
 template <int MODE, int KIND>
 static hipError_t launch_lds_ms(int ms, int m_tiles, const GemmArgs& g, hipStream_t st) {
   const int ncols = (MODE == EPI_SWIGLU) ? g.N / 128 : (g.N + NB - 1) / NB;
   const dim3 grid(ncols, m_tiles);
-  if (ms <= 2) launch_lds_variant<2, MODE, KIND, LDS_ROWB, LDS_NST, LDS_PF>(grid, g, st);
-  else if (ms <= 4 || KIND == KIND_FP8) launch_lds_variant<4, MODE, KIND, LDS_ROWB, LDS_NST, LDS_PF>(grid, g, st);
-  else launch_lds_variant<8, MODE, KIND, LDS_ROWB, LDS_NST, LDS_PF>(grid, g, st);
+  if constexpr (KIND == KIND_FP8) {
+    if (ms <= 4) launch_lds_variant<4, MODE, KIND, 2, 4, 128, 2>(grid, g, st);
+    else launch_lds_variant<8, MODE, KIND, 2, 4, 128, 2>(grid, g, st);
+  } else {
+    if (ms <= 2) launch_lds_variant<2, MODE, KIND, 2, 2, 128, 2>(grid, g, st);
+    else if (ms <= 4) launch_lds_variant<4, MODE, KIND, 2, 2, 128, 2>(grid, g, st);
+    else launch_lds_variant<8, MODE, KIND, 2, 2, 128, 2>(grid, g, st);
+  }
   return hipGetLastError();
 }
 

@@ -117,8 +117,8 @@ moe_status_t to_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR
 
 }  // namespace
 
-// Experts with at least 128 rows run on the LDS-staged kernel (bf16: 256-row
-// tiles, fp8: 128); experts with fewer rows, every decode-sized expert and the
+// Experts with at least 128 rows run on the LDS-staged kernel (256-row tiles);
+// experts with fewer rows, every decode-sized expert and the
 // MXFP4 recipe run on the register-streaming kernel with 32- or 64-row tiles.
 FfnPlan ffn_plan(const moe_config_t& c) {
   FfnPlan p{};
@@ -134,7 +134,7 @@ FfnPlan ffn_plan(const moe_config_t& c) {
   const int64_t avg = P / std::max<int64_t>(1, E);
   p.bm_s = avg <= 40 ? 32 : 64;
   p.thresh = (c.recipe == MOE_RECIPE_MXFP4) ? INT32_MAX : 128;
-  p.bm_l = (c.recipe == MOE_RECIPE_BF16) ? 256 : 128;
+  p.bm_l = 256;
   p.max_l = (p.thresh == INT32_MAX || P < p.thresh) ? 0 : int((P + p.bm_l - 1) / p.bm_l + std::min<int64_t>(E, P / p.thresh));
   const int64_t small_bound = (p.thresh == INT32_MAX) ? (P + p.bm_s - 1) / p.bm_s + E
                                                       : E * ((p.thresh + p.bm_s - 1) / p.bm_s);
