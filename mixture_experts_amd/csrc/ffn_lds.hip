@@ -176,8 +176,10 @@ __device__ __forceinline__ void stage_fp8(f32x4 (&acc)[MU][NC], const uint8_t* A
   }
 }
 
-// MS: 32-row fragments per tile; WM x WN: wavefront grid.
-template <int MS, int MODE, int KIND, int WM, int WN>
+// MS: 32-row fragments per tile; WM x WN: wavefront grid; PIPE (bf16 only): 1 =
+// the stage barrier sits before the stage's last sub-step, so that stage k+2's
+// copies and stage k+1's first LDS reads overlap stage k's last MFMAs.
+template <int MS, int MODE, int KIND, int WM, int WN, int PIPE = 0>
 __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
   constexpr int NW = WM * WN;                       // wavefronts
   constexpr int BM = MS * 32;
@@ -348,8 +350,80 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
     }
   };
 
-  // ---- main loop: stage kt is consumed from slot kt % NST while stage kt+1 lands
   const int KT = K / KS;
+  if constexpr (PIPE == 1 && !FP8) {
+    // ---- bf16 main loop, barrier before the last sub-step.  Every wave runs it,
+    // also one without real rows (its copies and barriers are shared).
+    constexpr int NS = ROWB / 32;
+    const int half = lane >> 5, l32 = lane & 31;
+    auto mainloop = [&](auto njc) {
+      constexpr int NJ = decltype(njc)::value;
+      constexpr int NJA = NJ > 0 ? NJ : 1;
+      bf16x8 bv[2][NF], av[2][NJA];
+      auto rd = [&](auto bufc, int s, int slot) {
+        constexpr int bb = decltype(bufc)::value;
+        if constexpr (NJ > 0) {
+          const int off = l32 * ROWB + (swz_slot(l32, 2 * s + half) << 4);
+          const uint8_t* Aw = (bb == 0 ? As0 : As1) + wm * 32 * ROWB + off;
+          const uint8_t* Bw = (bb == 0 ? Bs0 : Bs1) + brow0 * ROWB + off;
+#pragma unroll
+          for (int f = 0; f < NF; ++f) bv[slot][f] = __builtin_bit_cast(bf16x8, lds16(Bw + bfrag_row<SPLIT>(f) * ROWB));
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) av[slot][j] = __builtin_bit_cast(bf16x8, lds16(Aw + WM * 32 * ROWB * j));
+        }
+      };
+      auto mm = [&](int slot) {
+        if constexpr (NJ > 0) {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int f = 0; f < NF; ++f)
+              acc16[j][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[slot][j], bv[slot][f], acc16[j][f], 0, 0, 0);
+        }
+      };
+      // stage kt from slot bb; stage kt+1 is landing in the other slot
+      auto step = [&](int kt, auto bufc) {
+        constexpr int bb = decltype(bufc)::value;
+#pragma unroll
+        for (int s = 0; s < NS - 1; ++s) {
+          rd(bufc, s + 1, (s + 1) & 1);
+          sched_fence();
+          mm(s & 1);
+          sched_fence();
+        }
+        if (kt + 1 < KT) {
+          wait_vmcnt<0>();                            // stage kt+1 has landed (own copies)
+          __syncthreads();                            // (everyone's); everyone is done reading stage kt
+          if (kt + 2 < KT) issue((kt + 2) * KS, bb);
+        }
+        rd(std::integral_constant<int, bb ^ 1>{}, 0, 0);   // (after the last stage: unused)
+        sched_fence();
+        mm((NS - 1) & 1);
+        sched_fence();
+      };
+      rd(std::integral_constant<int, 0>{}, 0, 0);
+      int kt = 0;
+      for (; kt + 1 < KT; kt += 2) {
+        step(kt, std::integral_constant<int, 0>{});
+        step(kt + 1, std::integral_constant<int, 1>{});
+      }
+      if (kt < KT) step(kt, std::integral_constant<int, 0>{});
+    };
+    issue(0, 0);
+    if (KT > 1) {
+      issue(KS, 1);
+      wait_vmcnt<PER_STAGE>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+    if (MW >= 4 && nj == 4) mainloop(std::integral_constant<int, (MW >= 4 ? 4 : 0)>{});
+    else if (MW >= 3 && nj == 3) mainloop(std::integral_constant<int, (MW >= 3 ? 3 : 0)>{});
+    else if (MW >= 2 && nj == 2) mainloop(std::integral_constant<int, (MW >= 2 ? 2 : 0)>{});
+    else if (nj == 1) mainloop(std::integral_constant<int, 1>{});
+    else mainloop(std::integral_constant<int, 0>{});
+  } else {
+  // ---- main loop: stage kt is consumed from slot kt % NST while stage kt+1 lands
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
     if (s < KT) issue(s * KS, s);
@@ -372,6 +446,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
       if (kt + NST - 1 < KT) issue((kt + NST - 1) * KS, nb);
       compute(buf);
     }
+  }
   }
 
   // ---- epilogues
@@ -484,17 +559,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
   }
 }
 
-template <int MS, int MODE, int KIND, int WM, int WN>
+template <int MS, int MODE, int KIND, int WM, int WN, int PIPE = 0>
 void launch_lds_variant(dim3 grid, const GemmArgs& g, hipStream_t st) {
   static_assert(size_t(NST) * (MS * 32 + NB) * ROWB + size_t(NST + WN) * MS * 32 * 4 + 64 <= 160 * 1024, "LDS budget");
-  ffn_lds_kernel<MS, MODE, KIND, WM, WN><<<grid, 64 * WM * WN, 0, st>>>(g);
+  ffn_lds_kernel<MS, MODE, KIND, WM, WN, PIPE><<<grid, 64 * WM * WN, 0, st>>>(g);
 }
 
-// Production configurations.  bf16: 2 x 2 wavefronts, up to 256-row tiles (the
-// accumulators stay in the MFMA's own registers).  fp8: 2 x 4 wavefronts (two per
-// SIMD), 256-row tiles: the block-scale FMAs keep the accumulators in ordinary
-// VGPRs, and a second wave per SIMD overlaps one wave's FMAs with the other's
-// MFMAs.
+// Production configurations.  bf16: 256-row tiles on 2 x 4 wavefronts (two per
+// SIMD) with the stage barrier before the last sub-step; smaller tiles on 2 x 2
+// wavefronts.  fp8: 2 x 4 wavefronts, 256-row tiles: the block-scale FMAs keep
+// the accumulators in ordinary VGPRs, and a second wave per SIMD overlaps one
+// wave's FMAs with the other's MFMAs.
 template <int MODE, int KIND>
 static hipError_t launch_lds_ms(int ms, int m_tiles, const GemmArgs& g, hipStream_t st) {
   const int ncols = (MODE == EPI_SWIGLU) ? g.N / 128 : (g.N + NB - 1) / NB;
@@ -505,7 +580,7 @@ static hipError_t launch_lds_ms(int ms, int m_tiles, const GemmArgs& g, hipStrea
   } else {
     if (ms <= 2) launch_lds_variant<2, MODE, KIND, 2, 2>(grid, g, st);
     else if (ms <= 4) launch_lds_variant<4, MODE, KIND, 2, 2>(grid, g, st);
-    else launch_lds_variant<8, MODE, KIND, 2, 2>(grid, g, st);
+    else launch_lds_variant<8, MODE, KIND, 2, 4, 1>(grid, g, st);
   }
   return hipGetLastError();
 }
