@@ -38,7 +38,6 @@ namespace moe {
 
 namespace {
 
-constexpr int NB = 256;          // weight rows per tile
 constexpr int ROWB = 128;        // bytes of K per LDS row and stage
 constexpr int NST = 2;           // stages in the LDS ring
 
@@ -83,18 +82,25 @@ __device__ __forceinline__ float max_over_lanes16(float v) {   // within each 16
 
 }  // namespace
 
-// Row offset of weight fragment f within a wave's share of the tile's weight rows:
-// SwiGLU (SPLIT = gate fragments per wave) takes its gate fragments from rows
-// 0..127 and the matching up fragments from rows 128..255.
-template <int SPLIT>
-__device__ constexpr int bfrag_row(int f) { return SPLIT > 0 ? (f < SPLIT ? 0 : 128) + (f % SPLIT) * 32 : f * 32; }
+// Row offset of weight fragment f within a wave's share of the tile's NB weight
+// rows: SwiGLU (SPLIT = gate fragments per wave) takes its gate fragments from
+// rows 0..NB/2-1 and the matching up fragments from rows NB/2..NB-1.
+template <int SPLIT, int NB>
+__device__ constexpr int bfrag_row(int f) { return SPLIT > 0 ? (f < SPLIT ? 0 : NB / 2) + (f % SPLIT) * 32 : f * 32; }
+
+// fp8 scale staging (separate LDS variables, instantiated by the fp8 kernels only)
+template <int N, int ID>
+__device__ __forceinline__ float* lds_f32() {
+  __shared__ __attribute__((aligned(16))) float a[N];
+  return a;
+}
 
 // One bf16 stage (64 K) for the NJ row fragments of this wave that hold real rows,
 // in 16-deep sub-steps: the operands of sub-step s+1 are read from LDS while the
 // MFMAs of sub-step s run (register double buffer; the order is pinned with
 // scheduling barriers).  Every LDS row a wave reads is 32*m + l32, whose swizzle
 // key is l32's.  Aw / Bw: the wave's first A / weight row in this stage's slot.
-template <int NJ, int MW, int NF, int WM, int SPLIT>
+template <int NJ, int MW, int NF, int WM, int SPLIT, int NB>
 __device__ __forceinline__ void stage_bf16(f32x16 (&acc)[MW][NF], const uint8_t* Aw, const uint8_t* Bw, int l32,
                                            int half) {
   constexpr int NS = ROWB / 32;
@@ -102,7 +108,7 @@ __device__ __forceinline__ void stage_bf16(f32x16 (&acc)[MW][NF], const uint8_t*
   auto rd = [&](int s, int slot) {
     const int off = l32 * ROWB + (swz_slot(l32, 2 * s + half) << 4);   // k = 16s + 8h .. +8
 #pragma unroll
-    for (int f = 0; f < NF; ++f) bv[slot][f] = __builtin_bit_cast(bf16x8, lds16(Bw + bfrag_row<SPLIT>(f) * ROWB + off));
+    for (int f = 0; f < NF; ++f) bv[slot][f] = __builtin_bit_cast(bf16x8, lds16(Bw + bfrag_row<SPLIT, NB>(f) * ROWB + off));
 #pragma unroll
     for (int j = 0; j < NJ; ++j) av[slot][j] = __builtin_bit_cast(bf16x8, lds16(Aw + WM * 32 * ROWB * j + off));
   };
@@ -130,7 +136,7 @@ __device__ __forceinline__ void stage_bf16(f32x16 (&acc)[MW][NF], const uint8_t*
 // them, and the other wave of the SIMD fills that wait with its own MFMAs.
 // Sw: the stage's row scales; sbv: its two weight scales; sbi[f]: which one
 // fragment f takes.
-template <int NU, int MU, int NC, int WM, int SPLIT>
+template <int NU, int MU, int NC, int WM, int SPLIT, int NB>
 __device__ __forceinline__ void stage_fp8(f32x4 (&acc)[MU][NC], const uint8_t* As_buf, const uint8_t* Bw,
                                           const float* Sw, const float (&sbv)[2], const int (&sbi)[NC / 2], int wm,
                                           int r16, int kg) {
@@ -141,7 +147,7 @@ __device__ __forceinline__ void stage_fp8(f32x4 (&acc)[MU][NC], const uint8_t* A
   f32x4 part[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const uint8_t* p = Bw + (bfrag_row<SPLIT>(c >> 1) + 16 * (c & 1)) * ROWB;
+    const uint8_t* p = Bw + (bfrag_row<SPLIT, NB>(c >> 1) + 16 * (c & 1)) * ROWB;
     bv[c] = cat(lds16(p + lo0), lds16(p + lo1));
   }
   auto rd = [&](int u, int slot) {
@@ -178,13 +184,14 @@ __device__ __forceinline__ void stage_fp8(f32x4 (&acc)[MU][NC], const uint8_t* A
 
 // MS: 32-row fragments per tile; WM x WN: wavefront grid; PIPE (bf16 only): 1 =
 // the stage barrier sits before the stage's last sub-step, so that stage k+2's
-// copies and stage k+1's first LDS reads overlap stage k's last MFMAs.
-template <int MS, int MODE, int KIND, int WM, int WN, int PIPE = 0>
+// copies and stage k+1's first LDS reads overlap stage k's last MFMAs; NB: weight
+// rows per tile (SwiGLU: NB/2 h columns).
+template <int MS, int MODE, int KIND, int WM, int WN, int PIPE = 0, int NB = 256>
 __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
   constexpr int NW = WM * WN;                       // wavefronts
   constexpr int BM = MS * 32;
   constexpr int MW = MS / WM;                       // row fragments per wave
-  constexpr int NF = 8 / WN;                        // weight fragments per wave
+  constexpr int NF = NB / 32 / WN;                  // weight fragments per wave
   constexpr int NFG = NF / 2;                       // SwiGLU: gate (= up) fragments per wave
   constexpr int SPLIT = (MODE == EPI_SWIGLU) ? NFG : 0;
   constexpr int A_INSTR = BM * (ROWB / 16) / 64 / NW;   // async copies per wave per stage (A)
@@ -192,6 +199,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
   static_assert(MW >= 1 && NFG >= 1 && A_INSTR >= 1 && B_INSTR >= 1, "tile shape");
   static_assert(BM * (ROWB / 16) == A_INSTR * 64 * NW && NB * (ROWB / 16) == B_INSTR * 64 * NW, "copy cover");
   constexpr bool FP8 = KIND == KIND_FP8;
+  static_assert(!FP8 || NB == 256, "fp8 re-quantisation needs the tile's 128 h columns");
   constexpr int EB = FP8 ? 1 : 2;                   // bytes per element
   constexpr int KS = ROWB / EB;                     // K per stage
   // One LDS variable per ring slot and role: the compiler then knows that the
@@ -200,15 +208,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
   static_assert(NST == 2, "two ring slots");
   __shared__ __attribute__((aligned(1024))) uint8_t As0[BM * ROWB], As1[BM * ROWB];
   __shared__ __attribute__((aligned(1024))) uint8_t Bs0[NB * ROWB], Bs1[NB * ROWB];
-  __shared__ __attribute__((aligned(16))) float Sa0[FP8 ? BM : 4], Sa1[FP8 ? BM : 4];   // fp8 row scales
-  __shared__ float Sb0[4], Sb1[4];                                                      // fp8 weight scales
-  __shared__ __attribute__((aligned(16))) float amax_lds[FP8 ? WN * BM : 4];            // fp8 epilogue
+  float *Sa0 = nullptr, *Sa1 = nullptr, *Sb0 = nullptr, *Sb1 = nullptr, *amax_lds = nullptr;
+  if constexpr (FP8) {
+    Sa0 = lds_f32<BM, 0>();                          // row scales
+    Sa1 = lds_f32<BM, 1>();
+    Sb0 = lds_f32<4, 2>();                           // weight scales
+    Sb1 = lds_f32<4, 3>();
+    amax_lds = lds_f32<WN * BM, 4>();                // epilogue
+  }
   auto As = [&](int buf) -> uint8_t* { return buf == 0 ? As0 : As1; };
   auto Bs = [&](int buf) -> uint8_t* { return buf == 0 ? Bs0 : Bs1; };
   auto Sa = [&](int buf) -> float* { return buf == 0 ? Sa0 : Sa1; };
   auto Sb = [&](int buf) -> float* { return buf == 0 ? Sb0 : Sb1; };
 
-  const int ncols = (MODE == EPI_SWIGLU) ? g.N / 128 : (g.N + NB - 1) / NB;
+  const int ncols = (MODE == EPI_SWIGLU) ? g.N / (NB / 2) : (g.N + NB - 1) / NB;
   const int ntiles_m = g.tiles ? g.tiles[0] : (g.dense_rows + BM - 1) / BM;
   const int V = ncols * ntiles_m;
   const int b = blockIdx.y * gridDim.x + blockIdx.x;
@@ -244,7 +257,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
   }
   int n0, sub0 = 0;
   if (MODE == EPI_SWIGLU) {
-    n0 = nt * 128;
+    n0 = nt * (NB / 2);
     sub0 = ti.e * g.n_experts_split + n0 / ns;
   } else {
     n0 = nt * NB;
@@ -256,7 +269,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
     const int c = swz_slot(r, p % (ROWB / 16));
     size_t rowoff;
     if (MODE == EPI_SWIGLU) {
-      const int wr = (r < 128) ? (n0 % ns + r) : (ns + n0 % ns + r - 128);
+      const int wr = (r < NB / 2) ? (n0 % ns + r) : (ns + n0 % ns + r - NB / 2);
       rowoff = (size_t(sub0) * 2 * ns + wr) * size_t(K);
     } else {
       const int n = min(n0 + r, g.N - 1);
@@ -274,9 +287,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
   // 1 up block; down: q = 128-column block of the tile's 256 columns).
   float sa_reg[NST], sb_reg[NST];
   auto issue = [&](int k0, int buf) {
+    // (a copy whose 8 rows all lie past the tile's real rows is skipped: its LDS
+    // rows only feed accumulator rows that are never stored)
 #pragma unroll
     for (int j = 0; j < A_INSTR; ++j)
-      async_copy16(a_src[j] + size_t(k0) * EB, As(buf) + (wave * A_INSTR + j) * 1024);
+      if ((wave * A_INSTR + j) * (1024 / ROWB) < ti.rows)
+        async_copy16(a_src[j] + size_t(k0) * EB, As(buf) + (wave * A_INSTR + j) * 1024);
     const size_t ko = koff_bytes(k0);
 #pragma unroll
     for (int j = 0; j < B_INSTR; ++j) async_copy16(b_src[j] + ko, Bs(buf) + (wave * B_INSTR + j) * 1024);
@@ -295,7 +311,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
       }
     }
   };
-  constexpr int PER_STAGE = A_INSTR + B_INSTR + (FP8 ? 2 : 0);   // loads per thread per stage
 
   // Tile-relative weight column of each of this wave's fragments (SwiGLU: the h
   // column block of the gate/up pair); the wave's first LDS weight row.
@@ -333,20 +348,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
     if constexpr (!FP8) {
       const int half = lane >> 5, l32 = lane & 31;
       const uint8_t* Aw = As(buf) + wm * 32 * ROWB;
-      if (MW >= 4 && nj == 4) stage_bf16<(MW >= 4 ? 4 : 1), MW, NF, WM, SPLIT>(acc16, Aw, Bw, l32, half);
-      else if (MW >= 3 && nj == 3) stage_bf16<(MW >= 3 ? 3 : 1), MW, NF, WM, SPLIT>(acc16, Aw, Bw, l32, half);
-      else if (MW >= 2 && nj == 2) stage_bf16<(MW >= 2 ? 2 : 1), MW, NF, WM, SPLIT>(acc16, Aw, Bw, l32, half);
-      else if (nj == 1) stage_bf16<1, MW, NF, WM, SPLIT>(acc16, Aw, Bw, l32, half);
+      if (MW >= 4 && nj == 4) stage_bf16<(MW >= 4 ? 4 : 1), MW, NF, WM, SPLIT, NB>(acc16, Aw, Bw, l32, half);
+      else if (MW >= 3 && nj == 3) stage_bf16<(MW >= 3 ? 3 : 1), MW, NF, WM, SPLIT, NB>(acc16, Aw, Bw, l32, half);
+      else if (MW >= 2 && nj == 2) stage_bf16<(MW >= 2 ? 2 : 1), MW, NF, WM, SPLIT, NB>(acc16, Aw, Bw, l32, half);
+      else if (nj == 1) stage_bf16<1, MW, NF, WM, SPLIT, NB>(acc16, Aw, Bw, l32, half);
     } else {
       const int r16 = lane & 15, kg = lane >> 4;
       const uint8_t* Ab = As(buf);
       const float* Sw = Sa(buf);
       const float sbv[2] = {Sb(buf)[0], Sb(buf)[1]};
       constexpr int MU = 2 * MW, NC = 2 * NF;
-      if (MW >= 4 && nj == 4) stage_fp8<(MW >= 4 ? 8 : 2), MU, NC, WM, SPLIT>(acc4, Ab, Bw, Sw, sbv, sbi, wm, r16, kg);
-      else if (MW >= 3 && nj == 3) stage_fp8<(MW >= 3 ? 6 : 2), MU, NC, WM, SPLIT>(acc4, Ab, Bw, Sw, sbv, sbi, wm, r16, kg);
-      else if (MW >= 2 && nj == 2) stage_fp8<(MW >= 2 ? 4 : 2), MU, NC, WM, SPLIT>(acc4, Ab, Bw, Sw, sbv, sbi, wm, r16, kg);
-      else if (nj == 1) stage_fp8<2, MU, NC, WM, SPLIT>(acc4, Ab, Bw, Sw, sbv, sbi, wm, r16, kg);
+      if (MW >= 4 && nj == 4) stage_fp8<(MW >= 4 ? 8 : 2), MU, NC, WM, SPLIT, NB>(acc4, Ab, Bw, Sw, sbv, sbi, wm, r16, kg);
+      else if (MW >= 3 && nj == 3) stage_fp8<(MW >= 3 ? 6 : 2), MU, NC, WM, SPLIT, NB>(acc4, Ab, Bw, Sw, sbv, sbi, wm, r16, kg);
+      else if (MW >= 2 && nj == 2) stage_fp8<(MW >= 2 ? 4 : 2), MU, NC, WM, SPLIT, NB>(acc4, Ab, Bw, Sw, sbv, sbi, wm, r16, kg);
+      else if (nj == 1) stage_fp8<2, MU, NC, WM, SPLIT, NB>(acc4, Ab, Bw, Sw, sbv, sbi, wm, r16, kg);
     }
   };
 
@@ -367,7 +382,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
           const uint8_t* Aw = (bb == 0 ? As0 : As1) + wm * 32 * ROWB + off;
           const uint8_t* Bw = (bb == 0 ? Bs0 : Bs1) + brow0 * ROWB + off;
 #pragma unroll
-          for (int f = 0; f < NF; ++f) bv[slot][f] = __builtin_bit_cast(bf16x8, lds16(Bw + bfrag_row<SPLIT>(f) * ROWB));
+          for (int f = 0; f < NF; ++f) bv[slot][f] = __builtin_bit_cast(bf16x8, lds16(Bw + bfrag_row<SPLIT, NB>(f) * ROWB));
 #pragma unroll
           for (int j = 0; j < NJ; ++j) av[slot][j] = __builtin_bit_cast(bf16x8, lds16(Aw + WM * 32 * ROWB * j));
         }
@@ -410,12 +425,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
       if (kt < KT) step(kt, std::integral_constant<int, 0>{});
     };
     issue(0, 0);
-    if (KT > 1) {
-      issue(KS, 1);
-      wait_vmcnt<PER_STAGE>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    if (KT > 1) issue(KS, 1);
+    wait_vmcnt<0>();                                // (a wave's copy count varies with the tile's rows)
     __syncthreads();
     if (MW >= 4 && nj == 4) mainloop(std::integral_constant<int, (MW >= 4 ? 4 : 0)>{});
     else if (MW >= 3 && nj == 3) mainloop(std::integral_constant<int, (MW >= 3 ? 3 : 0)>{});
@@ -432,10 +443,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
     for (int buf = 0; buf < NST; ++buf) {            // unrolled: the ring slot is a constant
       const int kt = kt0 + buf;
       if (kt >= KT) break;
-      // wait until stage kt has landed (later stages may still be in flight)
-      const int ahead = min(NST - 2, KT - 1 - kt);
-      if (NST >= 3 && ahead >= 1) wait_vmcnt<(NST >= 3 ? PER_STAGE : 0)>();
-      else wait_vmcnt<0>();
+      wait_vmcnt<0>();                              // stage kt has landed (own copies)
       if (FP8) {
         if (tid < BM) Sa(buf)[tid] = sa_reg[buf];
         if (tid < 2) Sb(buf)[tid] = sb_reg[buf];
@@ -559,10 +567,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
   }
 }
 
-template <int MS, int MODE, int KIND, int WM, int WN, int PIPE = 0>
-void launch_lds_variant(dim3 grid, const GemmArgs& g, hipStream_t st) {
-  static_assert(size_t(NST) * (MS * 32 + NB) * ROWB + size_t(NST + WN) * MS * 32 * 4 + 64 <= 160 * 1024, "LDS budget");
-  ffn_lds_kernel<MS, MODE, KIND, WM, WN, PIPE><<<grid, 64 * WM * WN, 0, st>>>(g);
+template <int MS, int MODE, int KIND, int WM, int WN, int PIPE = 0, int NB = 256>
+void launch_lds_variant(const GemmArgs& g, int m_tiles, hipStream_t st) {
+  constexpr size_t lds = size_t(NST) * (MS * 32 + NB) * ROWB + (KIND == KIND_FP8 ? size_t(NST + WN) * MS * 32 * 4 + 32 : 0);
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  const int ncols = (MODE == EPI_SWIGLU) ? g.N / (NB / 2) : (g.N + NB - 1) / NB;
+  ffn_lds_kernel<MS, MODE, KIND, WM, WN, PIPE, NB><<<dim3(ncols, m_tiles), 64 * WM * WN, 0, st>>>(g);
 }
 
 // Production configurations.  bf16: 256-row tiles on 2 x 4 wavefronts (two per
@@ -572,15 +582,13 @@ void launch_lds_variant(dim3 grid, const GemmArgs& g, hipStream_t st) {
 // wave's FMAs with the other's MFMAs.
 template <int MODE, int KIND>
 static hipError_t launch_lds_ms(int ms, int m_tiles, const GemmArgs& g, hipStream_t st) {
-  const int ncols = (MODE == EPI_SWIGLU) ? g.N / 128 : (g.N + NB - 1) / NB;
-  const dim3 grid(ncols, m_tiles);
   if constexpr (KIND == KIND_FP8) {
-    if (ms <= 4) launch_lds_variant<4, MODE, KIND, 2, 4>(grid, g, st);
-    else launch_lds_variant<8, MODE, KIND, 2, 4>(grid, g, st);
+    if (ms <= 4) launch_lds_variant<4, MODE, KIND, 2, 4>(g, m_tiles, st);
+    else launch_lds_variant<8, MODE, KIND, 2, 4>(g, m_tiles, st);
   } else {
-    if (ms <= 2) launch_lds_variant<2, MODE, KIND, 2, 2>(grid, g, st);
-    else if (ms <= 4) launch_lds_variant<4, MODE, KIND, 2, 2>(grid, g, st);
-    else launch_lds_variant<8, MODE, KIND, 2, 4, 1>(grid, g, st);
+    if (ms <= 2) launch_lds_variant<2, MODE, KIND, 2, 2>(g, m_tiles, st);
+    else if (ms <= 4) launch_lds_variant<4, MODE, KIND, 2, 2>(g, m_tiles, st);
+    else launch_lds_variant<8, MODE, KIND, 2, 4, 1>(g, m_tiles, st);
   }
   return hipGetLastError();
 }
