@@ -16,18 +16,28 @@ namespace moe {
 // rounded FP32 linear layer except when the fp64 sum lands within ~1e-16
 // (relative) of an fp32 rounding boundary.
 //
-// fp64 MFMA 16x16x4: a 64x64 (token x expert) tile per 256-thread block; each
-// wave owns a 32x32 quarter = 2x2 MFMA tiles.  K is staged through LDS in
-// chunks of 32, converted to fp64 once on the way in.
+// fp64 MFMA 16x16x4: a 128 x 64 (token x expert) tile per 256-thread block; wave w
+// owns tokens 32w .. 32w+31 against all 64 experts (2 x 4 MFMA tiles).  K runs in
+// chunks of 32, staged through LDS as fp32 (bf16 widens exactly) in a two-slot
+// ring: the next chunk's global loads (16 bytes per lane) are in flight while the
+// current chunk is multiplied.  Within a chunk, lane group g = lane / 16 takes
+// k = 8g .. 8g+7 over the chunk's 8 MFMA steps (the same K order for both
+// operands), so that each lane reads its 8 k of a row with two 16-byte LDS reads.
 // ---------------------------------------------------------------------------
-constexpr int GT = 64, GE = 64, GK = 32, GPAD = GK + 1;
+constexpr int GT = 128, GE = 64, GK = 32, GPAD = GK + 4;   // 144-byte LDS rows: conflict-free 16-lane reads
 
 template <typename XT>
-__device__ __forceinline__ double load_x64(const XT* p);
+struct GateLoad;
 template <>
-__device__ __forceinline__ double load_x64<float>(const float* p) { return double(*p); }
+struct GateLoad<uint16_t> {                        // bf16 x: 8 values (16 bytes) per load, 2 loads per thread
+  static constexpr int PER_ROW = GK / 8, N = GT * PER_ROW / 256;
+  uint4 v[N];
+};
 template <>
-__device__ __forceinline__ double load_x64<uint16_t>(const uint16_t* p) { return double(bf16_to_f32(*p)); }
+struct GateLoad<float> {                           // fp32 x: 4 values per load, 4 loads per thread
+  static constexpr int PER_ROW = GK / 4, N = GT * PER_ROW / 256;
+  float4 v[N];
+};
 
 // Split over K (blockIdx.z) when there are too few (token, expert) tiles to fill
 // the chip: each split writes fp64 partial sums, which the router adds in a fixed
@@ -36,58 +46,105 @@ template <typename XT>
 __global__ __launch_bounds__(256) void gate_logits_f64(const XT* __restrict__ x, const float* __restrict__ wg,
                                                        float* __restrict__ logits, double* __restrict__ partial,
                                                        int T, int E, int H, int kchunk) {
-  __shared__ double As[GT][GPAD];
-  __shared__ double Bs[GE][GPAD];
+  __shared__ __attribute__((aligned(16))) float As[2][GT][GPAD];
+  __shared__ __attribute__((aligned(16))) float Bs[2][GE][GPAD];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r16 = lane & 15, g = lane >> 4;
   const int t0 = blockIdx.y * GT, e0 = blockIdx.x * GE;
-  const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;
-  f64x4 acc[2][2];
+  const int kbeg = blockIdx.z * kchunk, nch = kchunk / GK;
+
+  // global -> register loads of one chunk (rows past T / E read row 0 and store 0)
+  using LA = GateLoad<XT>;
+  LA la;
+  float4 lb[2];                                     // Wg: 64 rows x 8 segments of 4 floats
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < LA::N; ++i) {
+      const int idx = tid + 256 * i, row = idx / LA::PER_ROW, seg = idx % LA::PER_ROW;
+      const int t = min(t0 + row, T - 1);
+      if constexpr (sizeof(XT) == 2) la.v[i] = *reinterpret_cast<const uint4*>(x + size_t(t) * H + k0 + seg * 8);
+      else la.v[i] = *reinterpret_cast<const float4*>(x + size_t(t) * H + k0 + seg * 4);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 256 * i, row = idx / 8, seg = idx % 8;
+      const int e = min(e0 + row, E - 1);
+      lb[i] = *reinterpret_cast<const float4*>(wg + size_t(e) * H + k0 + seg * 4);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LA::N; ++i) {
+      const int idx = tid + 256 * i, row = idx / LA::PER_ROW, seg = idx % LA::PER_ROW;
+      const bool ok = t0 + row < T;
+      if constexpr (sizeof(XT) == 2) {
+        const uint32_t w[4] = {la.v[i].x, la.v[i].y, la.v[i].z, la.v[i].w};
+        float f[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f[2 * q] = ok ? __uint_as_float(w[q] << 16) : 0.0f;
+          f[2 * q + 1] = ok ? __uint_as_float(w[q] & 0xffff0000u) : 0.0f;
+        }
+        *reinterpret_cast<float4*>(&As[buf][row][seg * 8]) = make_float4(f[0], f[1], f[2], f[3]);
+        *reinterpret_cast<float4*>(&As[buf][row][seg * 8 + 4]) = make_float4(f[4], f[5], f[6], f[7]);
+      } else {
+        *reinterpret_cast<float4*>(&As[buf][row][seg * 4]) = ok ? la.v[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 256 * i, row = idx / 8, seg = idx % 8;
+      const bool ok = e0 + row < E;
+      *reinterpret_cast<float4*>(&Bs[buf][row][seg * 4]) = ok ? lb[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+
+  f64x4 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
 
-  // loader mapping: thread -> (row = tid / 4, 8 consecutive k at (tid % 4) * 8)
-  const int lr = tid >> 2, lk = (tid & 3) * 8;
-  const int kbeg = blockIdx.z * kchunk, kend = kbeg + kchunk;
-  for (int k0 = kbeg; k0 < kend; k0 += GK) {
-    {
-      const int t = t0 + lr;
-      const bool ok = t < T;
-      const XT* src = x + size_t(ok ? t : 0) * H + k0 + lk;
+  load(kbeg);
+  store(0);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nch) load(kbeg + (c + 1) * GK);     // in flight during this chunk's MFMAs
+    float a[2][8], b[4][8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) As[lr][lk + q] = ok ? load_x64<XT>(src + q) : 0.0;
-      const int e = e0 + lr;
-      const bool oke = e < E;
-      const float* wsrc = wg + size_t(oke ? e : 0) * H + k0 + lk;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) Bs[lr][lk + q] = oke ? double(wsrc[q]) : 0.0;
+    for (int i = 0; i < 2; ++i) {
+      const float* p = &As[buf][wave * 32 + 16 * i + r16][8 * g];
+      const float4 lo = *reinterpret_cast<const float4*>(p), hi = *reinterpret_cast<const float4*>(p + 4);
+      a[i][0] = lo.x; a[i][1] = lo.y; a[i][2] = lo.z; a[i][3] = lo.w;
+      a[i][4] = hi.x; a[i][5] = hi.y; a[i][6] = hi.z; a[i][7] = hi.w;
     }
-    __syncthreads();
 #pragma unroll
-    for (int s = 0; s < GK / 4; ++s) {
-      const int kk = s * 4 + (lane >> 4);
-      double a[2], b[2];
+    for (int j = 0; j < 4; ++j) {
+      const float* p = &Bs[buf][16 * j + r16][8 * g];
+      const float4 lo = *reinterpret_cast<const float4*>(p), hi = *reinterpret_cast<const float4*>(p + 4);
+      b[j][0] = lo.x; b[j][1] = lo.y; b[j][2] = lo.z; b[j][3] = lo.w;
+      b[j][4] = hi.x; b[j][5] = hi.y; b[j][6] = hi.z; b[j][7] = hi.w;
+    }
 #pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = As[wr + i * 16 + (lane & 15)][kk];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = Bs[wc + j * 16 + (lane & 15)][kk];
+    for (int q = 0; q < 8; ++q)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(a[i][q]), double(b[j][q]), acc[i][j], 0, 0, 0);
+    if (c + 1 < nch) store(buf ^ 1);                 // the slot read in the previous chunk
     __syncthreads();
   }
   // D[i][j]: lane holds column j = lane % 16, rows 4 * r + lane / 16
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = t0 + wr + i * 16 + r * 4 + (lane >> 4);
-        const int e = e0 + wc + j * 16 + (lane & 15);
+        const int t = t0 + wave * 32 + i * 16 + r * 4 + g;
+        const int e = e0 + j * 16 + r16;
         if (t < T && e < E) {
           if (partial) partial[(size_t(blockIdx.z) * T + t) * E + e] = acc[i][j][r];
           else logits[size_t(t) * E + e] = float(acc[i][j][r]);
@@ -217,7 +274,7 @@ int gate_ksplit(const moe_config_t& c) {
   const int tiles = ((c.num_experts + GE - 1) / GE) * ((c.num_tokens + GT - 1) / GT);
   const int steps = c.hidden / GK;
   int best = 1;
-  for (int d = 1; d <= steps && d <= 64; ++d)
+  for (int d = 1; d <= steps && d <= 32; ++d)
     if (steps % d == 0 && tiles * d <= 512) best = d;
   return best;
 }
