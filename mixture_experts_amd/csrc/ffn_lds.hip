@@ -253,7 +253,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
   for (int j = 0; j < A_INSTR; ++j) {
     const int p = (wave * A_INSTR + j) * 64 + lane, r = p / (ROWB / 16);
     const int c = swz_slot(r, p % (ROWB / 16));
-    a_src[j] = A + size_t(ti.row0 + min(r, ti.rows - 1)) * g.lda * EB + c * 16;
+    a_src[j] = A + size_t(a_row(g, ti.row0 + min(r, ti.rows - 1))) * g.lda * EB + c * 16;
   }
   int n0, sub0 = 0;
   if (MODE == EPI_SWIGLU) {
@@ -286,6 +286,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
   // tid % BM; sb = weight scale q = tid & 1 of the tile (SwiGLU: q = 0 gate block,
   // 1 up block; down: q = 128-column block of the tile's 256 columns).
   float sa_reg[NST], sb_reg[NST];
+  const int sa_row = FP8 ? a_row(g, ti.row0 + min(tid % BM, ti.rows - 1)) : 0;   // this thread's A-scale row
   auto issue = [&](int k0, int buf) {
     // (a copy whose 8 rows all lie past the tile's real rows is skipped: its LDS
     // rows only feed accumulator rows that are never stored)
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
     for (int j = 0; j < B_INSTR; ++j) async_copy16(b_src[j] + ko, Bs(buf) + (wave * B_INSTR + j) * 1024);
     if (FP8) {
       const float* SA = static_cast<const float*>(g.A_scale);
-      sa_reg[buf] = SA[size_t(ti.row0 + min(tid % BM, ti.rows - 1)) * (K / 128) + k0 / 128];
+      sa_reg[buf] = SA[size_t(sa_row) * (K / 128) + k0 / 128];
       const float* SB = static_cast<const float*>(g.B_scale);
       const int q = tid & 1;
       if (MODE == EPI_SWIGLU) {

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(GemmArgs g) {
   const int r = threadIdx.x >> 4;
   const int col = blockIdx.x * 16 + (threadIdx.x & 15);
   if (r >= ti.rows || col >= g.N) return;
-  const float* A = static_cast<const float*>(g.A) + size_t(ti.row0 + r) * g.lda;
+  const float* A = static_cast<const float*>(g.A) + size_t(a_row(g, ti.row0 + r)) * g.lda;
   const float* B = static_cast<const float*>(g.B);
   const int K = g.K, ns = g.nsplit;
   if (MODE == EPI_SWIGLU) {

@@ -142,13 +142,13 @@ __global__ __launch_bounds__(256) void ffn_rs_kernel(GemmArgs g) {
 #pragma unroll
   for (int j = 0; j < A_INSTR; ++j) {
     const int p = (wave * A_INSTR + j) * 64 + lane, r = p >> 3, c = rs_slot(r, p & 7);
-    a_src[j] = A + size_t(ti.row0 + min(r, ti.rows - 1)) * g.lda * EA + c * 16;
+    a_src[j] = A + size_t(a_row(g, ti.row0 + min(r, ti.rows - 1))) * g.lda * EA + c * 16;
   }
+  const int sa_row = BF16 ? 0 : a_row(g, ti.row0 + min(tid % BM, ti.rows - 1));
   auto load_sa = [&](int k0) -> uint32_t {        // every thread loads (rows clamped): equal vmcnt per wave
-    const int r = min(tid % BM, ti.rows - 1);
     if (MX) return *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(g.A_scale) +
-                                                      size_t(ti.row0 + r) * (K / 32) + k0 / 32);
-    return __float_as_uint(static_cast<const float*>(g.A_scale)[size_t(ti.row0 + r) * (K / 128) + k0 / 128]);
+                                                      size_t(sa_row) * (K / 32) + k0 / 32);
+    return __float_as_uint(static_cast<const float*>(g.A_scale)[size_t(sa_row) * (K / 128) + k0 / 128]);
   };
 
   uint4 breg[NST][2][BCH];

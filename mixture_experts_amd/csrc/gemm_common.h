@@ -27,6 +27,11 @@ struct GemmArgs {
   void* out_scale;          // h scales for the quantised recipes
   int ldo;
   int out_f32;              // down projection: store fp32 instead of bf16
+  // Fused gather: when a_map is set, the A row (and A-scale row) of pair row p is
+  // a_map[p] / a_div -- the token of the p-th sorted (token, slot) pair -- so the
+  // GEMM reads the token rows directly instead of a gathered copy.
+  const int32_t* a_map;
+  int a_div;
   // combine epilogue
   const void* y_perm;
   const int32_t* pair_pos;
@@ -53,6 +58,9 @@ __device__ __forceinline__ bool get_tile(const GemmArgs& g, int BM, TileInfo& ti
   }
   return ti.rows > 0;
 }
+
+// A-operand row of pair row p (see GemmArgs::a_map).
+__device__ __forceinline__ int a_row(const GemmArgs& g, int p) { return g.a_map ? g.a_map[p] / g.a_div : p; }
 
 // 32x32 MFMA accumulator layout: register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }

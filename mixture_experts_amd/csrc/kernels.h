@@ -29,6 +29,7 @@ hipError_t launch_route(const moe_config_t& c, const void* x, const float* gate_
 hipError_t launch_permute(const moe_config_t& c, const int32_t* topk_idx, const void* x, int32_t* offsets,
                           int32_t* sorted_pair, int32_t* pair_pos, void* x_perm, void* x_perm_scale,
                           int32_t* hist_ws, hipStream_t st);
+hipError_t launch_quantize_tokens(const moe_config_t& c, const void* x, void* xq, void* xq_scale, hipStream_t st);
 
 // Scratch of the grouped FFN: tile lists + SwiGLU output h (+ its scales).
 struct FfnScratch {
@@ -47,8 +48,10 @@ struct FfnPlan {
 };
 FfnPlan ffn_plan(const moe_config_t& c);
 
+// a_map (nullable): pair row p reads activation row a_map[p] / top_k of x_perm (the
+// fused gather: x_perm then holds the token rows in token order).
 hipError_t launch_grouped_ffn(const moe_config_t& c, const int32_t* offsets, const void* x_perm,
-                              const void* x_perm_scale, const moe_weights_t& w, void* y_perm,
+                              const void* x_perm_scale, const int32_t* a_map, const moe_weights_t& w, void* y_perm,
                               const FfnScratch& s, hipStream_t st);
 
 hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32_t* pair_pos, const float* topk_w,

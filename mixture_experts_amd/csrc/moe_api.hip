@@ -143,7 +143,7 @@ FfnPlan ffn_plan(const moe_config_t& c) {
 }
 
 hipError_t launch_grouped_ffn(const moe_config_t& c, const int32_t* offsets, const void* x_perm,
-                              const void* x_perm_scale, const moe_weights_t& w, void* y_perm,
+                              const void* x_perm_scale, const int32_t* a_map, const moe_weights_t& w, void* y_perm,
                               const FfnScratch& s, hipStream_t st) {
   const FfnPlan fp = ffn_plan(c);
   hipError_t e;
@@ -156,6 +156,8 @@ hipError_t launch_grouped_ffn(const moe_config_t& c, const int32_t* offsets, con
   GemmArgs g{};
   g.A = x_perm;
   g.A_scale = x_perm_scale;
+  g.a_map = a_map;
+  g.a_div = c.top_k;
   g.lda = c.hidden;
   g.offsets = offsets;
   g.B = w.w13;
@@ -187,6 +189,7 @@ hipError_t launch_grouped_ffn(const moe_config_t& c, const int32_t* offsets, con
   GemmArgs d = g;
   d.A = s.h;
   d.A_scale = s.h_scale;
+  d.a_map = nullptr;                                   // h rows are in pair order
   d.lda = c.intermediate;
   d.B = w.w2;
   d.B_scale = w.w2_scale;
@@ -385,7 +388,7 @@ moe_status_t moe_grouped_ffn(const moe_config_t* cfg, const int32_t* expert_offs
   if (quantised(*cfg) && !x_perm_scale) return MOE_ERR_INVALID_ARGUMENT;
   const Layout L = layout(*cfg);
   FfnScratch sc{at<int32_t>(ws, L.tiles_l), at<int32_t>(ws, L.tiles_s), at<void>(ws, L.h), at<void>(ws, L.h_scale)};
-  return to_status(launch_grouped_ffn(*cfg, expert_offsets, x_perm, x_perm_scale, *experts, y_perm, sc,
+  return to_status(launch_grouped_ffn(*cfg, expert_offsets, x_perm, x_perm_scale, nullptr, *experts, y_perm, sc,
                                       static_cast<hipStream_t>(stream)));
 }
 
@@ -418,13 +421,15 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* ga
   void* x_perm = at<void>(ws, L.x_perm);
   void* x_perm_scale = quantised(c) ? at<void>(ws, L.x_perm_scale) : nullptr;
   void* y_perm = at<void>(ws, L.y_perm);
+  int32_t* sorted = at<int32_t>(ws, L.sorted);
   hipError_t e = launch_route(c, x, gate_w, bias, idx, w, at<float>(ws, L.logits), at<double>(ws, L.gate_partial), st);
-  if (e == hipSuccess)
-    e = launch_permute(c, idx, x, offsets, at<int32_t>(ws, L.sorted), pos, x_perm, x_perm_scale,
-                       at<int32_t>(ws, L.hist), st);
+  // Fused gather: the routed GEMMs read the token rows of x (or of its quantised
+  // copy, made once per token) through the sorted pair order, with no gathered copy.
+  if (e == hipSuccess) e = launch_permute(c, idx, x, offsets, sorted, pos, nullptr, nullptr, at<int32_t>(ws, L.hist), st);
+  if (e == hipSuccess && quantised(c)) e = launch_quantize_tokens(c, x, x_perm, x_perm_scale, st);
   if (e == hipSuccess) {
     FfnScratch sc{at<int32_t>(ws, L.tiles_l), at<int32_t>(ws, L.tiles_s), at<void>(ws, L.h), at<void>(ws, L.h_scale)};
-    e = launch_grouped_ffn(c, offsets, x_perm, x_perm_scale, *experts, y_perm, sc, st);
+    e = launch_grouped_ffn(c, offsets, quantised(c) ? x_perm : x, x_perm_scale, sorted, *experts, y_perm, sc, st);
   }
   if (e == hipSuccess)
     e = launch_combine(c, y_perm, pos, w, x, shared, out, at<void>(ws, L.h_shared), at<float>(ws, L.sh_out), st);

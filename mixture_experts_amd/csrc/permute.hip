@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void perm_gather(const void* __restrict__ xv, 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int p = blockIdx.x * 4 + wave;
   if (p >= pairs) return;
-  const int t = sorted_pair[p] / k;
+  const int t = sorted_pair ? sorted_pair[p] / k : p;   // (no pair order: quantise token rows in place order)
   if (RECIPE == MOE_RECIPE_F32) {
     const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(xv) + size_t(t) * H);
     float4* dst = reinterpret_cast<float4*>(static_cast<float*>(outv) + size_t(p) * H);
@@ -190,6 +190,18 @@ hipError_t launch_permute(const moe_config_t& c, const int32_t* topk_idx, const 
                                                           x_perm_scale);
     }
   }
+  return hipGetLastError();
+}
+
+// Activation quantisation of the token rows in token order (the fused-gather path:
+// the grouped GEMMs then read row token(p) of this copy for pair row p).
+hipError_t launch_quantize_tokens(const moe_config_t& c, const void* x, void* xq, void* xq_scale, hipStream_t st) {
+  ProfScope p(MOE_K_GATHER, st);
+  const int g = (c.num_tokens + 3) / 4;
+  if (c.recipe == MOE_RECIPE_FP8_B128)
+    perm_gather<MOE_RECIPE_FP8_B128><<<g, 256, 0, st>>>(x, nullptr, c.num_tokens, 1, c.hidden, xq, xq_scale);
+  else if (c.recipe == MOE_RECIPE_MXFP4)
+    perm_gather<MOE_RECIPE_MXFP4><<<g, 256, 0, st>>>(x, nullptr, c.num_tokens, 1, c.hidden, xq, xq_scale);
   return hipGetLastError();
 }
 
