@@ -2,6 +2,8 @@
 // weighted put-back sum of the routed rows (plus the shared-expert rows).
 // moe_infer per-expert MLP and put-back: DeepSeek-V3 walk-through
 // (pwwt.cn/news/5781524), section 3.4.
+#include <algorithm>
+
 #include "gemm_common.h"
 #include "kernels.h"
 
@@ -102,9 +104,11 @@ hipError_t launch_f32(int mode, int m_tiles, const GemmArgs& g, hipStream_t st) 
 //   out[t] = sum_j w[t][j] * y_perm[pair_pos[t*k+j]] (+ sh[t]), fp32 accumulation.
 // One workgroup per token; each thread owns 8 consecutive channels (16-byte loads).
 // ---------------------------------------------------------------------------
+// sh: nsh fp32 slabs [T][H], sh_stride elements apart, summed in order (K-split
+// partial products of the shared expert's down projection; nsh = 1: its rows).
 __global__ __launch_bounds__(256) void combine_bf16(const uint16_t* __restrict__ yp, const int32_t* __restrict__ pair_pos,
-                                                    const float* __restrict__ w, const float* __restrict__ sh, int k,
-                                                    int H, uint16_t* __restrict__ out) {
+                                                    const float* __restrict__ w, const float* __restrict__ sh, int nsh,
+                                                    size_t sh_stride, int k, int H, uint16_t* __restrict__ out) {
   __shared__ int32_t pos[16];
   __shared__ float wt[16];
   const int t = blockIdx.x;
@@ -115,13 +119,12 @@ __global__ __launch_bounds__(256) void combine_bf16(const uint16_t* __restrict__
   __syncthreads();
   for (int c = threadIdx.x; c < H / 8; c += 256) {
     float acc[8];
-    if (sh) {
-      const float4 a = reinterpret_cast<const float4*>(sh + size_t(t) * H)[2 * c];
-      const float4 b = reinterpret_cast<const float4*>(sh + size_t(t) * H)[2 * c + 1];
-      acc[0] = a.x; acc[1] = a.y; acc[2] = a.z; acc[3] = a.w; acc[4] = b.x; acc[5] = b.y; acc[6] = b.z; acc[7] = b.w;
-    } else {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+    for (int z = 0; z < nsh; ++z) {
+      const float4* src = reinterpret_cast<const float4*>(sh + z * sh_stride + size_t(t) * H);
+      const float4 a = src[2 * c], b = src[2 * c + 1];
+      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w; acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
     }
     for (int j = 0; j < k; ++j) {
       const uint4 v = reinterpret_cast<const uint4*>(yp + size_t(pos[j]) * H)[c];
@@ -152,15 +155,49 @@ __global__ __launch_bounds__(256) void combine_f32(const float* __restrict__ yp,
   }
 }
 
-// sh: fp32 shared-expert rows [T][H] or nullptr (bf16-output recipes only).
+// sh: nsh fp32 slabs of shared-expert rows [T][H] (bf16-output recipes only; nsh = 0: none).
 hipError_t launch_combine_rows(const moe_config_t& c, const void* y_perm, const int32_t* pair_pos,
-                               const float* topk_w, const float* sh, void* out, hipStream_t st) {
+                               const float* topk_w, const float* sh, int nsh, void* out, hipStream_t st) {
   if (c.recipe == MOE_RECIPE_F32)
     combine_f32<<<c.num_tokens, 256, 0, st>>>(static_cast<const float*>(y_perm), pair_pos, topk_w, c.top_k,
                                               c.hidden, static_cast<float*>(out));
   else
-    combine_bf16<<<c.num_tokens, 256, 0, st>>>(static_cast<const uint16_t*>(y_perm), pair_pos, topk_w, sh, c.top_k,
-                                               c.hidden, static_cast<uint16_t*>(out));
+    combine_bf16<<<c.num_tokens, 256, 0, st>>>(static_cast<const uint16_t*>(y_perm), pair_pos, topk_w, sh, nsh,
+                                               size_t(c.num_tokens) * c.hidden, c.top_k, c.hidden,
+                                               static_cast<uint16_t*>(out));
+  return hipGetLastError();
+}
+
+// SwiGLU of K-split gate/up partial products: part holds nz fp32 slabs [T][nes*2*Is]
+// (sub-expert s: gate columns s*2Is .. +Is, up columns s*2Is+Is .. +Is), summed in
+// order; h[t][s*Is + c] = bf16(SiLU(gate) * up).
+__global__ __launch_bounds__(256) void swiglu_slabs(const float* __restrict__ part, int nz, int T, int nes, int Is,
+                                                    uint16_t* __restrict__ h) {
+  const int SI = nes * Is;
+  const size_t stride = size_t(T) * 2 * SI;
+  const size_t n4 = size_t(T) * SI / 4;
+  for (size_t q = size_t(blockIdx.x) * 256 + threadIdx.x; q < n4; q += size_t(gridDim.x) * 256) {
+    const size_t i = q * 4;
+    const int t = int(i / SI), col = int(i % SI), s = col / Is, c = col % Is;
+    const size_t gi = size_t(t) * 2 * SI + size_t(s) * 2 * Is + c;
+    float4 gs = make_float4(0.f, 0.f, 0.f, 0.f), us = gs;
+    for (int z = 0; z < nz; ++z) {
+      const float4 gv = *reinterpret_cast<const float4*>(part + z * stride + gi);
+      const float4 uv = *reinterpret_cast<const float4*>(part + z * stride + gi + Is);
+      gs.x += gv.x; gs.y += gv.y; gs.z += gv.z; gs.w += gv.w;
+      us.x += uv.x; us.y += uv.y; us.z += uv.z; us.w += uv.w;
+    }
+    uint2 o;
+    o.x = uint32_t(f32_to_bf16(silu_f32(gs.x) * us.x)) | (uint32_t(f32_to_bf16(silu_f32(gs.y) * us.y)) << 16);
+    o.y = uint32_t(f32_to_bf16(silu_f32(gs.z) * us.z)) | (uint32_t(f32_to_bf16(silu_f32(gs.w) * us.w)) << 16);
+    *reinterpret_cast<uint2*>(h + i) = o;
+  }
+}
+
+hipError_t launch_swiglu_slabs(const float* part, int nz, int T, int nes, int Is, uint16_t* h, hipStream_t st) {
+  const size_t n4 = size_t(T) * nes * Is / 4;
+  const int blocks = int(std::min<size_t>((n4 + 255) / 256, 2048));
+  swiglu_slabs<<<blocks, 256, 0, st>>>(part, nz, T, nes, Is, h);
   return hipGetLastError();
 }
 

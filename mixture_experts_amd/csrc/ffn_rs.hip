@@ -179,10 +179,12 @@ __global__ __launch_bounds__(256) void ffn_rs_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
 
-  const int KT = K / KS;
+  // this block's K stages (a K split only in the plain store mode)
+  const int nz = (MODE == EPI_STORE) ? int(gridDim.z) : 1;
+  const int KT = K / KS / nz, kb = (MODE == EPI_STORE) ? int(blockIdx.z) * KT : 0;
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
-    if (s < KT) issue(s * KS, s);
+    if (s < KT) issue((kb + s) * KS, s);
 
   for (int kt0 = 0; kt0 < KT; kt0 += NST) {
 #pragma unroll
@@ -196,7 +198,7 @@ __global__ __launch_bounds__(256) void ffn_rs_kernel(GemmArgs g) {
       if (!BF16 && tid < BM) Sa[buf][tid] = sreg[buf];
       __syncthreads();
       const int nb = (buf + NST - 1) % NST;
-      if (kt + NST - 1 < KT) issue((kt + NST - 1) * KS, nb);
+      if (kt + NST - 1 < KT) issue((kb + kt + NST - 1) * KS, nb);
       if (!wave_on) continue;
       const uint8_t* Ab = As[buf];
       if (BF16) {
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(256) void ffn_rs_kernel(GemmArgs g) {
           }
         }
       } else if (FP8) {
-        const float sb0 = bscale_fp8(0, kt * KS), sb1 = bscale_fp8(1, kt * KS);
+        const float sb0 = bscale_fp8(0, (kb + kt) * KS), sb1 = bscale_fp8(1, (kb + kt) * KS);
 #pragma unroll
         for (int i = 0; i < MS; ++i) {
           if (i >= act_ms) continue;
@@ -344,7 +346,7 @@ __global__ __launch_bounds__(256) void ffn_rs_kernel(GemmArgs g) {
           const int row = i * 32 + acc_row(r, lane);
           if (row >= ti.rows) continue;
           const size_t o = size_t(ti.row0 + row) * g.ldo + col;
-          if (g.out_f32) static_cast<float*>(g.out)[o] = acc[i][f][r];
+          if (g.out_f32) static_cast<float*>(g.out)[blockIdx.z * g.split_stride + o] = acc[i][f][r];
           else static_cast<uint16_t*>(g.out)[o] = f32_to_bf16(acc[i][f][r]);
         }
       }
@@ -374,8 +376,10 @@ static hipError_t rs_launch_recipe(int recipe, int ms, dim3 grid, const GemmArgs
 hipError_t launch_rs_swiglu(int recipe, int ms, int m_tiles, const GemmArgs& g, hipStream_t st) {
   return rs_launch_recipe<EPI_SWIGLU>(recipe, ms, dim3(g.N / 128, m_tiles), g, st);
 }
-hipError_t launch_rs_down(int recipe, int ms, int m_tiles, const GemmArgs& g, hipStream_t st) {
-  return rs_launch_recipe<EPI_STORE>(recipe, ms, dim3((g.N + RS_NB - 1) / RS_NB, m_tiles), g, st);
+// ksplit > 1: fp32 partial products of ksplit equal K ranges (K / 64 / ksplit stages
+// each, an integer), see GemmArgs::split_stride.
+hipError_t launch_rs_down(int recipe, int ms, int m_tiles, const GemmArgs& g, hipStream_t st, int ksplit) {
+  return rs_launch_recipe<EPI_STORE>(recipe, ms, dim3((g.N + RS_NB - 1) / RS_NB, m_tiles, ksplit), g, st);
 }
 
 }  // namespace moe

@@ -32,6 +32,10 @@ struct GemmArgs {
   // GEMM reads the token rows directly instead of a gathered copy.
   const int32_t* a_map;
   int a_div;
+  // K split (register-streaming kernel, plain store mode): blockIdx.z takes the
+  // z-th of gridDim.z equal K ranges and writes its fp32 partial products to
+  // out + z * split_stride.
+  size_t split_stride;
   // combine epilogue
   const void* y_perm;
   const int32_t* pair_pos;

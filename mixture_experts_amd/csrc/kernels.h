@@ -56,6 +56,6 @@ hipError_t launch_grouped_ffn(const moe_config_t& c, const int32_t* offsets, con
 
 hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32_t* pair_pos, const float* topk_w,
                           const void* x, const moe_weights_t* shared, void* out, void* h_shared, float* sh_out,
-                          hipStream_t st);
+                          float* sh_part, hipStream_t st);
 
 }  // namespace moe

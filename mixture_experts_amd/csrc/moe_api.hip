@@ -10,10 +10,11 @@
 namespace moe {
 
 hipError_t launch_rs_swiglu(int recipe, int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
-hipError_t launch_rs_down(int recipe, int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
+hipError_t launch_rs_down(int recipe, int ms, int m_tiles, const GemmArgs& g, hipStream_t st, int ksplit);
 hipError_t launch_f32(int mode, int m_tiles, const GemmArgs& g, hipStream_t st);
 hipError_t launch_combine_rows(const moe_config_t& c, const void* y_perm, const int32_t* pair_pos,
-                               const float* topk_w, const float* sh, void* out, hipStream_t st);
+                               const float* topk_w, const float* sh, int nsh, void* out, hipStream_t st);
+hipError_t launch_swiglu_slabs(const float* part, int nz, int T, int nes, int Is, uint16_t* h, hipStream_t st);
 hipError_t launch_build_tiles2(const int32_t* offsets, int E, int thresh, int bm_large, int bm_small,
                                int32_t* tiles_l, int32_t* tiles_s, hipStream_t st);
 hipError_t launch_lds_swiglu(bool fp8, int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
@@ -56,10 +57,38 @@ size_t act_scale_bytes(const moe_config_t& c, int64_t rows, int64_t cols) {
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+int shared_ms(int T) { return T > 32 ? 2 : 1; }   // register-streaming tiles for small token counts
+
+// Shared expert at small token counts (decode): its two GEMMs have too few output
+// tiles to fill the chip, so each runs as ks equal K ranges writing fp32 partial
+// products (summed in order by the SwiGLU and the combine kernels).
+struct SharedSplit {
+  bool on;
+  int ms, mt, ks1, ks2;   // row-tile size (x32), row tiles, K splits of gate/up and of down
+};
+SharedSplit shared_split(const moe_config_t& c) {
+  SharedSplit s{};
+  const int T = c.num_tokens, SI = c.num_shared * c.shared_intermediate;
+  if (c.recipe == MOE_RECIPE_F32 || SI == 0 || T == 0 || T > 256) return s;
+  s.on = true;
+  s.ms = shared_ms(T);
+  s.mt = (T + 32 * s.ms - 1) / (32 * s.ms);
+  // largest split (<= 16) with whole 64-deep stages, >= 4 stages each, <= 1024 blocks
+  auto pick = [&](int ncols, int stages) {
+    int best = 1;
+    for (int d = 1; d <= 16; ++d)
+      if (stages % d == 0 && stages / d >= 4 && int64_t(ncols) * s.mt * d <= 1024) best = d;
+    return best;
+  };
+  s.ks1 = pick(2 * SI / 256, c.hidden / 64);
+  s.ks2 = pick((c.hidden + 255) / 256, SI / 64);
+  return s;
+}
+
 // Scratch layout; the same for every entry point so one size serves all of them.
 struct Layout {
-  size_t logits, gate_partial, hist, tiles_l, tiles_s, h, h_scale, h_shared, sh_out, idx, w, offsets, sorted, pos, x_perm, x_perm_scale, y_perm,
-      total;
+  size_t logits, gate_partial, hist, tiles_l, tiles_s, h, h_scale, h_shared, sh_out, sh_part, idx, w, offsets, sorted,
+      pos, x_perm, x_perm_scale, y_perm, total;
 };
 
 Layout layout(const moe_config_t& c) {
@@ -79,6 +108,8 @@ Layout layout(const moe_config_t& c) {
   L.h_scale = take(act_scale_bytes(c, P, I));
   L.h_shared = take(size_t(T * SI) * act_bytes(c));
   L.sh_out = take(c.recipe == MOE_RECIPE_F32 || SI == 0 ? 0 : size_t(T * H * 4));   // fp32 shared-expert rows
+  const SharedSplit ss = shared_split(c);
+  L.sh_part = take(ss.on ? size_t(std::max<int64_t>(ss.ks1 * T * 2 * SI, ss.ks2 * T * H)) * 4 : 0);
   L.idx = take(size_t(P * 4));
   L.w = take(size_t(P * 4));
   L.offsets = take(size_t((E + 1) * 4));
@@ -93,8 +124,6 @@ Layout layout(const moe_config_t& c) {
 
 template <typename T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
-
-int shared_ms(int T) { return T > 32 ? 2 : 1; }   // register-streaming tiles for small token counts
 
 moe_status_t check_common(const moe_config_t* c, void* ws, size_t ws_bytes) {
   if (!valid_config(c)) return MOE_ERR_INVALID_ARGUMENT;
@@ -210,17 +239,63 @@ hipError_t launch_grouped_ffn(const moe_config_t& c, const int32_t* offsets, con
     if (e != hipSuccess) return e;
   }
   d.tiles = s.tiles_s;
-  return launch_rs_down(c.recipe, fp.bm_s / 32, fp.max_s, d, st);
+  return launch_rs_down(c.recipe, fp.bm_s / 32, fp.max_s, d, st, 1);
 }
 
 hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32_t* pair_pos, const float* topk_w,
                           const void* x, const moe_weights_t* shared, void* out, void* h_shared, float* sh_out,
-                          hipStream_t st) {
+                          float* sh_part, hipStream_t st) {
   if (c.num_shared == 0) {
     ProfScope p(MOE_K_COMBINE, st);
-    return launch_combine_rows(c, y_perm, pair_pos, topk_w, nullptr, out, st);
+    return launch_combine_rows(c, y_perm, pair_pos, topk_w, nullptr, 0, out, st);
   }
   const int T = c.num_tokens, SI = c.num_shared * c.shared_intermediate;
+  hipError_t e;
+  const SharedSplit ss = shared_split(c);
+  if (ss.on) {
+    // gate/up rows of all shared experts as one [2*SI][H] matrix, K split
+    GemmArgs g{};
+    g.A = x;
+    g.lda = c.hidden;
+    g.dense_rows = T;
+    g.B = shared->w13;
+    g.K = c.hidden;
+    g.N = 2 * SI;
+    g.nsplit = c.hidden;
+    g.n_experts_split = 1;
+    g.out = sh_part;
+    g.ldo = 2 * SI;
+    g.out_f32 = 1;
+    g.split_stride = size_t(T) * 2 * SI;
+    {
+      ProfScope p(MOE_K_SHARED_GATE_UP, st);
+      e = launch_rs_down(MOE_RECIPE_BF16, ss.ms, ss.mt, g, st, ss.ks1);
+      if (e == hipSuccess)
+        e = launch_swiglu_slabs(sh_part, ss.ks1, T, c.num_shared, c.shared_intermediate,
+                                static_cast<uint16_t*>(h_shared), st);
+    }
+    if (e != hipSuccess) return e;
+    GemmArgs d{};
+    d.A = h_shared;
+    d.lda = SI;
+    d.dense_rows = T;
+    d.B = shared->w2;
+    d.K = SI;
+    d.N = c.hidden;
+    d.nsplit = c.shared_intermediate;
+    d.n_experts_split = c.num_shared;
+    d.out = sh_part;
+    d.ldo = c.hidden;
+    d.out_f32 = 1;
+    d.split_stride = size_t(T) * c.hidden;
+    {
+      ProfScope p(MOE_K_SHARED_DOWN_COMBINE, st);
+      e = launch_rs_down(MOE_RECIPE_BF16, ss.ms, ss.mt, d, st, ss.ks2);
+    }
+    if (e != hipSuccess) return e;
+    ProfScope p(MOE_K_COMBINE, st);
+    return launch_combine_rows(c, y_perm, pair_pos, topk_w, sh_part, ss.ks2, out, st);
+  }
   const bool f32 = c.recipe == MOE_RECIPE_F32;
   const bool lds = !f32 && T >= 128;                  // LDS-staged kernel for prefill-sized token counts
   const int ms = lds ? (T >= 256 ? 8 : 4) : shared_ms(T);
@@ -236,7 +311,6 @@ hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32
   g.n_experts_split = c.num_shared;
   g.out = h_shared;
   g.ldo = SI;
-  hipError_t e;
   {
     ProfScope p(MOE_K_SHARED_GATE_UP, st);
     e = f32 ? launch_f32(EPI_SWIGLU, mt, g, st)
@@ -263,11 +337,11 @@ hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32
   d.out_f32 = 1;
   {
     ProfScope p(MOE_K_SHARED_DOWN_COMBINE, st);
-    e = lds ? launch_lds_down(false, ms, mt, d, st) : launch_rs_down(MOE_RECIPE_BF16, ms, mt, d, st);
+    e = lds ? launch_lds_down(false, ms, mt, d, st) : launch_rs_down(MOE_RECIPE_BF16, ms, mt, d, st, 1);
   }
   if (e != hipSuccess) return e;
   ProfScope p(MOE_K_COMBINE, st);
-  return launch_combine_rows(c, y_perm, pair_pos, topk_w, sh_out, out, st);
+  return launch_combine_rows(c, y_perm, pair_pos, topk_w, sh_out, 1, out, st);
 }
 
 // ---------------------------------------------------------------- instrumentation
@@ -401,7 +475,7 @@ moe_status_t moe_combine(const moe_config_t* cfg, const void* y_perm, const int3
   if (cfg->num_shared > 0 && (!x || !shared || !shared->w13 || !shared->w2)) return MOE_ERR_INVALID_ARGUMENT;
   const Layout L = layout(*cfg);
   return to_status(launch_combine(*cfg, y_perm, pair_pos, topk_w, x, shared, out, at<void>(ws, L.h_shared),
-                                  at<float>(ws, L.sh_out), static_cast<hipStream_t>(stream)));
+                                  at<float>(ws, L.sh_out), at<float>(ws, L.sh_part), static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* gate_w, const float* bias,
@@ -432,7 +506,8 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* ga
     e = launch_grouped_ffn(c, offsets, quantised(c) ? x_perm : x, x_perm_scale, sorted, *experts, y_perm, sc, st);
   }
   if (e == hipSuccess)
-    e = launch_combine(c, y_perm, pos, w, x, shared, out, at<void>(ws, L.h_shared), at<float>(ws, L.sh_out), st);
+    e = launch_combine(c, y_perm, pos, w, x, shared, out, at<void>(ws, L.h_shared), at<float>(ws, L.sh_out),
+                       at<float>(ws, L.sh_part), st);
   return to_status(e);
 }
 
