@@ -188,7 +188,17 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ l
     float logit;
     if (partial) {                                      // K-split gate: fixed-order fp64 sum, one rounding
       double z = 0.0;
-      for (int q = 0; q < nsplit; ++q) z += partial[(size_t(q) * T + t) * E + e];
+      const double* pp = partial + size_t(t) * E + e;
+      const size_t ps = size_t(T) * E;
+      int q = 0;
+      for (; q + 8 <= nsplit; q += 8) {                 // 8 loads in flight, then the in-order sum
+        double v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = pp[(q + u) * ps];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) z += v[u];
+      }
+      for (; q < nsplit; ++q) z += pp[q * ps];
       logit = float(z);
     } else {
       logit = lg[e];
