@@ -59,13 +59,6 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// Bijective map of a linear block index b < V to a tile number so that the blocks
-// one XCD runs (b % 8 fixed) cover a contiguous range of tile numbers.
-__device__ __forceinline__ int xcd_tile(int b, int V) {
-  const int q = V >> 3, r = V & 7, x = b & 7, l = b >> 3;
-  return (x < r) ? x * (q + 1) + l : r * (q + 1) + (x - r) * q + l;
-}
-
 enum Kind { KIND_BF16 = 0, KIND_FP8 = 1 };
 
 __device__ __forceinline__ i32x8 cat(uint4 lo, uint4 hi) {
@@ -222,22 +215,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
   auto Sb = [&](int buf) -> float* { return buf == 0 ? Sb0 : Sb1; };
 
   const int ncols = (MODE == EPI_SWIGLU) ? g.N / (NB / 2) : (g.N + NB - 1) / NB;
-  const int ntiles_m = g.tiles ? g.tiles[0] : (g.dense_rows + BM - 1) / BM;
-  const int V = ncols * ntiles_m;
+  const int V = ncols * row_tiles(g, BM);
   const int b = blockIdx.y * gridDim.x + blockIdx.x;
   if (b >= V) return;
   const int tnum = xcd_tile(b, V);
   const int mt = tnum / ncols, nt = tnum - mt * ncols;
   TileInfo ti;
-  if (g.tiles) {
-    ti.e = g.tiles[1 + 2 * mt];
-    ti.row0 = g.offsets[ti.e] + g.tiles[2 + 2 * mt];
-    ti.rows = min(BM, g.offsets[ti.e + 1] - ti.row0);
-  } else {
-    ti.e = 0;
-    ti.row0 = mt * BM;
-    ti.rows = min(BM, g.dense_rows - ti.row0);
-  }
+  tile_info(g, BM, mt, ti);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave % WM, wn = wave / WM;
   const int K = g.K, ns = g.nsplit;

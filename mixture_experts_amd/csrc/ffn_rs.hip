@@ -71,8 +71,15 @@ __global__ __launch_bounds__(256) void ffn_rs_kernel(GemmArgs g) {
   __shared__ uint32_t Sa[NST][BM];                 // fp8: fp32 row scale bits; MX: 4 E8M0 bytes
   __shared__ float amax_lds[4][BM];
 
+  // (row tile, column block) pairs in XCD-major order: one expert's row tiles and
+  // column blocks run on one XCD, which then reads its weights and activations once
+  const int ncols = int(gridDim.x);
+  const int V = ncols * row_tiles(g, BM);
+  const int b = int(blockIdx.y) * ncols + int(blockIdx.x);
+  if (b >= V) return;
+  const int tnum = xcd_tile(b, V), mt = tnum / ncols, nt = tnum - mt * ncols;
   TileInfo ti;
-  if (!get_tile(g, BM, ti)) return;
+  if (!tile_info(g, BM, mt, ti)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
   const int K = g.K, ns = g.nsplit;
@@ -86,7 +93,7 @@ __global__ __launch_bounds__(256) void ffn_rs_kernel(GemmArgs g) {
   bool wave_on = true;
   int n0, sub0 = 0;
   if (MODE == EPI_SWIGLU) {
-    n0 = blockIdx.x * 128;
+    n0 = nt * 128;
     sub0 = ti.e * g.n_experts_split + n0 / ns;
     const int nl = n0 % ns + wave * 32 + l32;
     const size_t rowbytes = MX ? size_t(K) / 2 : size_t(K) * EBW;
@@ -96,7 +103,7 @@ __global__ __launch_bounds__(256) void ffn_rs_kernel(GemmArgs g) {
     ncol[0] = nl;
     ncol[1] = ns + nl;
   } else {
-    n0 = blockIdx.x * RS_NB;
+    n0 = nt * RS_NB;
     wave_on = n0 + wave * 64 < g.N;
     const int n = min(n0 + wave * 64 + l32, g.N - 1);
     const int n1 = min(n + 32, g.N - 1);

@@ -47,9 +47,10 @@ struct TileInfo {
   int e, row0, rows;
 };
 
-__device__ __forceinline__ bool get_tile(const GemmArgs& g, int BM, TileInfo& ti) {
+// Row tile `tile` of a launch: an (expert, first row) entry of the tile list, or a
+// BM-row slice of a dense operand.  False when the tile holds no rows.
+__device__ __forceinline__ bool tile_info(const GemmArgs& g, int BM, int tile, TileInfo& ti) {
   if (g.tiles) {
-    const int tile = blockIdx.y;
     if (tile >= g.tiles[0]) return false;
     ti.e = g.tiles[1 + 2 * tile];
     const int m0 = g.tiles[2 + 2 * tile];
@@ -57,10 +58,27 @@ __device__ __forceinline__ bool get_tile(const GemmArgs& g, int BM, TileInfo& ti
     ti.rows = min(BM, g.offsets[ti.e + 1] - ti.row0);
   } else {
     ti.e = 0;
-    ti.row0 = blockIdx.y * BM;
+    ti.row0 = tile * BM;
     ti.rows = min(BM, g.dense_rows - ti.row0);
   }
   return ti.rows > 0;
+}
+
+__device__ __forceinline__ bool get_tile(const GemmArgs& g, int BM, TileInfo& ti) {
+  return tile_info(g, BM, blockIdx.y, ti);
+}
+
+// Row tiles of a launch that holds them (the tile list's count, or the dense slices).
+__device__ __forceinline__ int row_tiles(const GemmArgs& g, int BM) {
+  return g.tiles ? g.tiles[0] : (g.dense_rows + BM - 1) / BM;
+}
+
+// Bijective map of a linear block index b < V to a tile number so that the blocks
+// one XCD runs (b % 8 fixed: workgroups are dealt round-robin over the eight XCDs)
+// cover a contiguous range of tile numbers and share that XCD's L2.
+__device__ __forceinline__ int xcd_tile(int b, int V) {
+  const int q = V >> 3, r = V & 7, x = b & 7, l = b >> 3;
+  return (x < r) ? x * (q + 1) + l : r * (q + 1) + (x - r) * q + l;
 }
 
 // A-operand row of pair row p (see GemmArgs::a_map).

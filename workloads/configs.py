@@ -143,8 +143,14 @@ MINI_PREFILL_FP8 = MoEConfig(
     score_func=SCORE_SQRTSOFTPLUS, routed_scaling_factor=2.5, recipe=RECIPE_FP8_B128,
     gate_std=1.0 / 16.0, description="prefill-shaped fp8 mini: 128-row tiles")
 
+MINI_MXFP4_WIDE = MoEConfig(
+    name="mini_mxfp4_wide", num_tokens=560, hidden=384, num_experts=16, top_k=4,
+    intermediate=256, num_shared=1, shared_intermediate=128,
+    recipe=RECIPE_MXFP4, gate_std=1.0 / 16.0,
+    description="MXFP4 mini with about 140 rows per expert: two or three ragged row tiles per expert")
+
 MINI_CONFIGS = [MINI_GROUPED_BF16, MINI_DECODE_BF16, MINI_MXFP4, MINI_FP8, MINI_F32, MINI_PREFILL_BF16,
-                MINI_PREFILL_FP8]
+                MINI_PREFILL_FP8, MINI_MXFP4_WIDE]
 
 BY_NAME = {c.name: c for c in FULL_CONFIGS + MINI_CONFIGS}
 
