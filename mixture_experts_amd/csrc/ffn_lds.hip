@@ -28,9 +28,10 @@
 // operands).
 //
 // Tiles are numbered (row tile, column tile), column tile fastest, and mapped so
-// that consecutive numbers run on the same XCD: column tiles sharing an
-// activation block, and the row tiles of one expert sharing weight rows, meet in
-// that XCD's L2.
+// that consecutive numbers run on the same XCD: the column tiles sharing an
+// activation block meet in that XCD's L2.  The row tiles of one expert read the
+// same weight rows, but far apart in time, so each of them streams the weights
+// from HBM again; experts of 257..511 rows therefore pay two weight passes.
 #include "gemm_common.h"
 #include "kernels.h"
 
