@@ -165,12 +165,16 @@ __device__ __forceinline__ void stage_fp8(f32x4 (&acc)[MU][NC], const uint8_t* A
   rd(0, 0);
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-    if (u + 1 < NU) rd(u + 1, (u + 1) & 1);
-    sched_fence();
+    // The unit's NC MFMAs back to back, then the next unit's LDS reads, then this
+    // unit's scale FMAs: each FMA reads an MFMA result that the later MFMAs' issue
+    // time has already covered, and the FMAs cover the LDS reads' latency.
 #pragma unroll
     for (int c = 0; c < NC; ++c)
       part[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[u & 1], bv[c], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0,
                                                                  127, 0, 127);
+    sched_fence();
+    if (u + 1 < NU) rd(u + 1, (u + 1) & 1);
+    sched_fence();
     fma_blk(u, u & 1);
     sched_fence();
   }
