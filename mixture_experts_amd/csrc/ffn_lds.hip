@@ -124,21 +124,25 @@ __device__ __forceinline__ void stage_bf16(f32x16 (&acc)[MW][NF], const uint8_t*
 // blocks of this wave that hold real rows.  Row block u: rows
 // (wm + WM*(u>>1))*32 + 16*(u&1) + 0..15; column block c = 2f + cb: weight
 // fragment f, columns 16*cb + 0..15.  Operand lane l: row / column l & 15, K bytes
-// 32*(l>>4) .. +32 of the stage (the same K order on both sides); accumulator
-// lane l, register r: row 4*(l>>4) + r, column l & 15.  The operands of row block
-// u+1 are read while the MFMAs of u run; the wave's FMAs on u's sums wait for
-// them, and the other wave of the SIMD fills that wait with its own MFMAs.
-// Sw: the stage's row scales; sbv: its two weight scales; sbi[f]: which one
-// fragment f takes.
+// 32*(l>>4) .. +32 of the stage (the same K order on both sides).  The weight
+// block is the MFMA's first operand, so accumulator lane l, register r holds
+// column 4*(l>>4) + r of token row l & 15: one row scale per lane and row block.
+// Sp: the stage's row scales, MU per lane in row-block order (see the kernel's
+// scale staging); sbv: its two weight scales; sbi[f]: which one fragment f takes.
 template <int NU, int MU, int NC, int WM, int SPLIT, int NB>
 __device__ __forceinline__ void stage_fp8(f32x4 (&acc)[MU][NC], const uint8_t* As_buf, const uint8_t* Bw,
-                                          const float* Sw, const float (&sbv)[2], const int (&sbi)[NC / 2], int wm,
+                                          const float* Sp, const float (&sbv)[2], const int (&sbi)[NC / 2], int wm,
                                           int r16, int kg) {
   const int lo0 = r16 * ROWB + (swz_slot(r16, 2 * kg) << 4);     // rows read are 16*m + r16
   const int lo1 = r16 * ROWB + (swz_slot(r16, 2 * kg + 1) << 4);
   i32x8 bv[NC], av[2];
-  float4 ra[2];
   f32x4 part[NC];
+  float sa[MU];
+#pragma unroll
+  for (int q = 0; q < MU / 4; ++q) {
+    const float4 v = *reinterpret_cast<const float4*>(Sp + (wm * 16 + r16) * MU + 4 * q);
+    sa[4 * q] = v.x; sa[4 * q + 1] = v.y; sa[4 * q + 2] = v.z; sa[4 * q + 3] = v.w;
+  }
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const uint8_t* p = Bw + (bfrag_row<SPLIT, NB>(c >> 1) + 16 * (c & 1)) * ROWB;
@@ -148,19 +152,13 @@ __device__ __forceinline__ void stage_fp8(f32x4 (&acc)[MU][NC], const uint8_t* A
     const int row = (wm + WM * (u >> 1)) * 32 + 16 * (u & 1);
     const uint8_t* p = As_buf + row * ROWB;
     av[slot] = cat(lds16(p + lo0), lds16(p + lo1));
-    ra[slot] = *reinterpret_cast<const float4*>(Sw + row + 4 * kg);
   };
-  auto fma_blk = [&](int u, int slot) {
-    const float rv[4] = {ra[slot].x, ra[slot].y, ra[slot].z, ra[slot].w};
-    float rs[2][4];
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) rs[q][r] = rv[r] * sbv[q];
+  auto fma_blk = [&](int u) {
+    const float rs[2] = {sa[u] * sbv[0], sa[u] * sbv[1]};
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[u][c][r] = fmaf(part[c][r], rs[sbi[c >> 1]][r], acc[u][c][r]);
+      for (int r = 0; r < 4; ++r) acc[u][c][r] = fmaf(part[c][r], rs[sbi[c >> 1]], acc[u][c][r]);
   };
   rd(0, 0);
 #pragma unroll
@@ -170,12 +168,12 @@ __device__ __forceinline__ void stage_fp8(f32x4 (&acc)[MU][NC], const uint8_t* A
     // time has already covered, and the FMAs cover the LDS reads' latency.
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      part[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[u & 1], bv[c], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0,
+      part[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv[c], av[u & 1], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0,
                                                                  127, 0, 127);
     sched_fence();
     if (u + 1 < NU) rd(u + 1, (u + 1) & 1);
     sched_fence();
-    fma_blk(u, u & 1);
+    fma_blk(u);
     sched_fence();
   }
 }
@@ -276,6 +274,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
   // 1 up block; down: q = 128-column block of the tile's 256 columns).
   float sa_reg[NST], sb_reg[NST];
   const int sa_row = FP8 ? a_row(g, ti.row0 + min(tid % BM, ti.rows - 1)) : 0;   // this thread's A-scale row
+  // LDS position of tile row tid's scale: lane r16 of the waves with row offset wm
+  // finds its MW*2 row blocks' scales at (wm*16 + r16)*2*MW + u
+  int sa_pos = 0;
+  if constexpr (FP8) {
+    const int r = tid % BM, i = r >> 5;
+    sa_pos = ((i % WM) * 16 + (r & 15)) * (2 * MW) + 2 * (i / WM) + ((r >> 4) & 1);
+  }
   auto issue = [&](int k0, int buf) {
     // (a copy whose 8 rows all lie past the tile's real rows is skipped: its LDS
     // rows only feed accumulator rows that are never stored)
@@ -345,13 +350,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
     } else {
       const int r16 = lane & 15, kg = lane >> 4;
       const uint8_t* Ab = As(buf);
-      const float* Sw = Sa(buf);
+      const float* Sp = Sa(buf);
       const float sbv[2] = {Sb(buf)[0], Sb(buf)[1]};
       constexpr int MU = 2 * MW, NC = 2 * NF;
-      if (MW >= 4 && nj == 4) stage_fp8<(MW >= 4 ? 8 : 2), MU, NC, WM, SPLIT, NB>(acc4, Ab, Bw, Sw, sbv, sbi, wm, r16, kg);
-      else if (MW >= 3 && nj == 3) stage_fp8<(MW >= 3 ? 6 : 2), MU, NC, WM, SPLIT, NB>(acc4, Ab, Bw, Sw, sbv, sbi, wm, r16, kg);
-      else if (MW >= 2 && nj == 2) stage_fp8<(MW >= 2 ? 4 : 2), MU, NC, WM, SPLIT, NB>(acc4, Ab, Bw, Sw, sbv, sbi, wm, r16, kg);
-      else if (nj == 1) stage_fp8<2, MU, NC, WM, SPLIT, NB>(acc4, Ab, Bw, Sw, sbv, sbi, wm, r16, kg);
+      if (MW >= 4 && nj == 4) stage_fp8<(MW >= 4 ? 8 : 2), MU, NC, WM, SPLIT, NB>(acc4, Ab, Bw, Sp, sbv, sbi, wm, r16, kg);
+      else if (MW >= 3 && nj == 3) stage_fp8<(MW >= 3 ? 6 : 2), MU, NC, WM, SPLIT, NB>(acc4, Ab, Bw, Sp, sbv, sbi, wm, r16, kg);
+      else if (MW >= 2 && nj == 2) stage_fp8<(MW >= 2 ? 4 : 2), MU, NC, WM, SPLIT, NB>(acc4, Ab, Bw, Sp, sbv, sbi, wm, r16, kg);
+      else if (nj == 1) stage_fp8<2, MU, NC, WM, SPLIT, NB>(acc4, Ab, Bw, Sp, sbv, sbi, wm, r16, kg);
     }
   };
 
@@ -435,7 +440,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
       if (kt >= KT) break;
       wait_vmcnt<0>();                              // stage kt has landed (own copies)
       if (FP8) {
-        if (tid < BM) Sa(buf)[tid] = sa_reg[buf];
+        if (tid < BM) Sa(buf)[sa_pos] = sa_reg[buf];
         if (tid < 2) Sb(buf)[tid] = sb_reg[buf];
       }
       __syncthreads();
@@ -490,66 +495,66 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
     }
   } else {
     // 16x16 accumulator layout: block (u, c) lane l register r -> tile row
-    // (wm + WM*(u>>1))*32 + 16*(u&1) + 4*(l>>4) + r, column fcol[c>>1] + 16*(c&1) + (l&15)
+    // (wm + WM*(u>>1))*32 + 16*(u&1) + (l&15), column fcol[c>>1] + 16*(c&1) + 4*(l>>4) + r
     constexpr int NC = 2 * NF;
     const int r16 = lane & 15, kg = lane >> 4;
     if (MODE == EPI_SWIGLU) {
       // h re-quantised per (row, 128 columns): the tile's 128 h columns are one
-      // block, split over the WN column waves
+      // block, split over the WN column waves and, within a wave, over the four
+      // lanes of a row
       uint8_t* Hq = static_cast<uint8_t*>(g.out);
 #pragma unroll
       for (int u = 0; u < 2 * MW; ++u) {
-        const int rb = (wm + WM * (u >> 1)) * 32 + 16 * (u & 1);
+        const int row = (wm + WM * (u >> 1)) * 32 + 16 * (u & 1) + r16;
         const bool on = (wm + WM * (u >> 1)) < act_ms;
         float hv[NC / 2][4];
+        float m = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float m = 0.0f;
+        for (int c = 0; c < NC / 2; ++c)
 #pragma unroll
-          for (int c = 0; c < NC / 2; ++c) {
+          for (int r = 0; r < 4; ++r) {
             hv[c][r] = silu_f32(acc4[u][c][r]) * acc4[u][c + NC / 2][r];
             m = fmaxf(m, fabsf(hv[c][r]));
           }
-          m = max_over_lanes16(m);
-          if (on && r16 == 0) amax_lds[wn * BM + rb + 4 * kg + r] = m;
-        }
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        if (on && kg == 0) amax_lds[wn * BM + row] = m;
         __syncthreads();
-        if (on) {
+        if (on && row < ti.rows) {
+          float amax = amax_lds[row];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = rb + 4 * kg + r;
-            float amax = amax_lds[row];
+          for (int q = 1; q < WN; ++q) amax = fmaxf(amax, amax_lds[q * BM + row]);
+          const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+          uint8_t* hrow = Hq + size_t(ti.row0 + row) * g.ldo + n0;
 #pragma unroll
-            for (int q = 1; q < WN; ++q) amax = fmaxf(amax, amax_lds[q * BM + row]);
-            const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-            if (row < ti.rows) {
+          for (int c = 0; c < NC / 2; ++c) {
+            uint32_t packed = 0;
 #pragma unroll
-              for (int c = 0; c < NC / 2; ++c)
-                Hq[size_t(ti.row0 + row) * g.ldo + n0 + fcol[c >> 1] + 16 * (c & 1) + r16] =
-                    uint8_t(f32_to_e4m3(hv[c][r] / s));
-              if (wn == 0 && r16 == 0)
-                static_cast<float*>(g.out_scale)[size_t(ti.row0 + row) * (g.N / 128) + n0 / 128] = s;
-            }
+            for (int r = 0; r < 4; ++r) packed |= uint32_t(f32_to_e4m3(hv[c][r] / sc)) << (8 * r);
+            *reinterpret_cast<uint32_t*>(hrow + fcol[c >> 1] + 16 * (c & 1) + 4 * kg) = packed;
           }
+          if (wn == 0 && kg == 0) static_cast<float*>(g.out_scale)[size_t(ti.row0 + row) * (g.N / 128) + n0 / 128] = sc;
         }
         __syncthreads();
       }
-    } else {  // EPI_STORE
+    } else {  // EPI_STORE: four consecutive columns per lane
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         if (n0 + fcol[c >> 1] >= g.N) continue;       // partial column tile (g.N % 128 == 0)
-        const int col = n0 + fcol[c >> 1] + 16 * (c & 1) + r16;
+        const int col = n0 + fcol[c >> 1] + 16 * (c & 1) + 4 * kg;
 #pragma unroll
         for (int u = 0; u < 2 * MW; ++u) {
           if ((wm + WM * (u >> 1)) >= act_ms) continue;
-          const int rb = (wm + WM * (u >> 1)) * 32 + 16 * (u & 1);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = rb + 4 * kg + r;
-            if (row >= ti.rows) continue;
-            const size_t o = size_t(ti.row0 + row) * g.ldo + col;
-            if (g.out_f32) static_cast<float*>(g.out)[o] = acc4[u][c][r];
-            else static_cast<uint16_t*>(g.out)[o] = f32_to_bf16(acc4[u][c][r]);
+          const int row = (wm + WM * (u >> 1)) * 32 + 16 * (u & 1) + r16;
+          if (row >= ti.rows) continue;
+          const size_t o = size_t(ti.row0 + row) * g.ldo + col;
+          if (g.out_f32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(g.out) + o) =
+                float4{acc4[u][c][0], acc4[u][c][1], acc4[u][c][2], acc4[u][c][3]};
+          } else {
+            const uint32_t lo = uint32_t(f32_to_bf16(acc4[u][c][0])) | (uint32_t(f32_to_bf16(acc4[u][c][1])) << 16);
+            const uint32_t hi = uint32_t(f32_to_bf16(acc4[u][c][2])) | (uint32_t(f32_to_bf16(acc4[u][c][3])) << 16);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.out) + o) = uint2{lo, hi};
           }
         }
       }
