@@ -55,8 +55,9 @@ __device__ __forceinline__ i32x8 rs_cat(uint4 lo, uint4 hi) {
 
 }  // namespace
 
-template <int MS, int MODE, int RECIPE, int NST>
-__global__ __launch_bounds__(256) void ffn_rs_kernel(GemmArgs g) {
+// WPE: minimum waves per SIMD the register allocation must leave room for.
+template <int MS, int MODE, int RECIPE, int NST, int WPE = 1>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void ffn_rs_kernel(GemmArgs g) {
   constexpr int BM = MS * 32;
   constexpr bool BF16 = RECIPE == MOE_RECIPE_BF16;
   constexpr bool MX = RECIPE == MOE_RECIPE_MXFP4;
@@ -366,6 +367,12 @@ constexpr int RS_NST1 = 2, RS_NST2 = 3;
 
 template <int MODE, int RECIPE>
 static void rs_launch(int ms, dim3 grid, const GemmArgs& g, hipStream_t st) {
+  if constexpr (RECIPE == MOE_RECIPE_MXFP4) {
+    if (ms >= 4) {                                 // 128-row tiles, held to two waves per SIMD
+      ffn_rs_kernel<4, MODE, RECIPE, 2, 2><<<grid, 256, 0, st>>>(g);
+      return;
+    }
+  }
   if (ms <= 1) ffn_rs_kernel<1, MODE, RECIPE, RS_NST1><<<grid, 256, 0, st>>>(g);
   else ffn_rs_kernel<2, MODE, RECIPE, RS_NST2><<<grid, 256, 0, st>>>(g);
 }
@@ -378,7 +385,7 @@ static hipError_t rs_launch_recipe(int recipe, int ms, dim3 grid, const GemmArgs
   return hipGetLastError();
 }
 
-// Tiles of ms*32 rows (ms = 1 or 2).  bf16 is used for the shared experts of every
+// Tiles of ms*32 rows (ms = 1 or 2; MXFP4 also 4).  bf16 is used for the shared experts of every
 // bf16-activation recipe as well.
 hipError_t launch_rs_swiglu(int recipe, int ms, int m_tiles, const GemmArgs& g, hipStream_t st) {
   return rs_launch_recipe<EPI_SWIGLU>(recipe, ms, dim3(g.N / 128, m_tiles), g, st);
