@@ -367,7 +367,7 @@ constexpr int RS_NST1 = 2, RS_NST2 = 3;
 
 template <int MODE, int RECIPE>
 static void rs_launch(int ms, dim3 grid, const GemmArgs& g, hipStream_t st) {
-  if constexpr (RECIPE == MOE_RECIPE_MXFP4) {
+  if constexpr (RECIPE != MOE_RECIPE_FP8_B128) {
     if (ms >= 4) {                                 // 128-row tiles, held to two waves per SIMD
       ffn_rs_kernel<4, MODE, RECIPE, 2, 2><<<grid, 256, 0, st>>>(g);
       return;
@@ -385,7 +385,7 @@ static hipError_t rs_launch_recipe(int recipe, int ms, dim3 grid, const GemmArgs
   return hipGetLastError();
 }
 
-// Tiles of ms*32 rows (ms = 1 or 2; MXFP4 also 4).  bf16 is used for the shared experts of every
+// Tiles of ms*32 rows (ms = 1 or 2; bf16 and MXFP4 also 4).  bf16 is used for the shared experts of every
 // bf16-activation recipe as well.
 hipError_t launch_rs_swiglu(int recipe, int ms, int m_tiles, const GemmArgs& g, hipStream_t st) {
   return rs_launch_recipe<EPI_SWIGLU>(recipe, ms, dim3(g.N / 128, m_tiles), g, st);

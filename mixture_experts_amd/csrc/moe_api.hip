@@ -148,8 +148,8 @@ moe_status_t to_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR
 
 // Experts with at least 128 rows run on the LDS-staged kernel (256-row tiles);
 // experts with fewer rows, every decode-sized expert and the
-// MXFP4 recipe run on the register-streaming kernel with 32- or 64-row tiles
-// (MXFP4: up to 128).
+// MXFP4 recipe run on the register-streaming kernel with 32-, 64- or (bf16 and
+// MXFP4) 128-row tiles.
 FfnPlan ffn_plan(const moe_config_t& c) {
   FfnPlan p{};
   const int64_t P = int64_t(c.num_tokens) * c.top_k, E = c.num_experts;
@@ -163,9 +163,11 @@ FfnPlan ffn_plan(const moe_config_t& c) {
   }
   const int64_t avg = P / std::max<int64_t>(1, E);
   p.bm_s = avg <= 40 ? 32 : 64;
-  // MXFP4 has no large-tile list: size its tiles so that a typical expert takes one
-  // tile and its weights stream from HBM once
+  // Size the register-streaming tiles so that a typical expert takes one tile and
+  // its weights stream from HBM once: MXFP4 has no large-tile list; bf16 sends only
+  // experts under 128 rows there.  (fp8's 128-row variant spills registers.)
   if (c.recipe == MOE_RECIPE_MXFP4) p.bm_s = avg <= 24 ? 32 : avg <= 48 ? 64 : 128;
+  else if (c.recipe == MOE_RECIPE_BF16 && avg > 48) p.bm_s = 128;
   p.thresh = (c.recipe == MOE_RECIPE_MXFP4) ? INT32_MAX : 128;
   p.bm_l = 256;
   p.max_l = (p.thresh == INT32_MAX || P < p.thresh) ? 0 : int((P + p.bm_l - 1) / p.bm_l + std::min<int64_t>(E, P / p.thresh));

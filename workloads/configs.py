@@ -149,8 +149,15 @@ MINI_MXFP4_WIDE = MoEConfig(
     recipe=RECIPE_MXFP4, gate_std=1.0 / 16.0,
     description="MXFP4 mini with about 140 rows per expert: two or three ragged row tiles per expert")
 
+MINI_MIXED_BF16 = MoEConfig(
+    name="mini_mixed_bf16", num_tokens=300, hidden=384, num_experts=24, top_k=6,
+    intermediate=256, num_shared=1, shared_intermediate=256,
+    routed_scaling_factor=2.5, recipe=RECIPE_BF16, gate_std=1.0 / 16.0, bias_kind="zipf", bias_param=1.1,
+    description="bf16 mini with a Zipf load: empty experts, 128-row register-streaming tiles and "
+                "256-row LDS tiles in one call, partial column tiles")
+
 MINI_CONFIGS = [MINI_GROUPED_BF16, MINI_DECODE_BF16, MINI_MXFP4, MINI_FP8, MINI_F32, MINI_PREFILL_BF16,
-                MINI_PREFILL_FP8, MINI_MXFP4_WIDE]
+                MINI_PREFILL_FP8, MINI_MXFP4_WIDE, MINI_MIXED_BF16]
 
 BY_NAME = {c.name: c for c in FULL_CONFIGS + MINI_CONFIGS}
 
