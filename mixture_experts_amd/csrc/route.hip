@@ -280,12 +280,27 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ l
 }
 
 // ---------------------------------------------------------------------------
+// K splits of the gate GEMM: the d (a divisor of the K chunks, <= 32) with the
+// least estimated time.  Two 128 x 64 blocks fit a CU (LDS), so a launch runs in
+// ceil(blocks / 512) rounds of K/d chunks each; every split beyond the first adds
+// a T x E fp64 partial written once and read once.  Per-chunk time and bandwidth
+// are round figures for the fp64 MFMA rate and HBM.
 int gate_ksplit(const moe_config_t& c) {
   const int tiles = ((c.num_experts + GE - 1) / GE) * ((c.num_tokens + GT - 1) / GT);
   const int steps = c.hidden / GK;
+  constexpr double chunk_s = 3.4e-6, bytes_per_s = 5e12;
   int best = 1;
-  for (int d = 1; d <= steps && d <= 32; ++d)
-    if (steps % d == 0 && tiles * d <= 512) best = d;
+  double best_t = 0.0;
+  for (int d = 1; d <= steps && d <= 32; ++d) {
+    if (steps % d) continue;
+    const double rounds = double((int64_t(tiles) * d + 511) / 512);
+    const double t = rounds * (steps / d) * chunk_s +
+                     (d > 1 ? double(d) * c.num_tokens * c.num_experts * 16.0 / bytes_per_s : 0.0);
+    if (d == 1 || t < 0.97 * best_t) {             // a split must win clearly
+      best = d;
+      best_t = t;
+    }
+  }
   return best;
 }
 
