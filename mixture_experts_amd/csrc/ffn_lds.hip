@@ -115,7 +115,7 @@ __device__ __forceinline__ void stage_bf16(f32x16 (&acc)[MW][NF], const uint8_t*
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int f = 0; f < NF; ++f)
-        acc[j][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s & 1][j], bv[s & 1][f], acc[j][f], 0, 0, 0);
+        acc[j][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[s & 1][f], av[s & 1][j], acc[j][f], 0, 0, 0);
     sched_fence();
   }
 }
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
           for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int f = 0; f < NF; ++f)
-              acc16[j][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[slot][j], bv[slot][f], acc16[j][f], 0, 0, 0);
+              acc16[j][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[slot][f], av[slot][j], acc16[j][f], 0, 0, 0);
         }
       };
       // stage kt from slot bb; stage kt+1 is landing in the other slot
@@ -454,22 +454,30 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
 
   // ---- epilogues
   if constexpr (!FP8) {
-    // 32x32 accumulator layout
-    const int l32 = lane & 31;
+    // 32x32 accumulator layout, weight fragment as the MFMA's first operand: lane
+    // l, register r = 4q + e holds token row l & 31 and column 8q + 4*(l>>5) + e of
+    // the fragment, so each lane stores runs of four consecutive columns
+    const int l32 = lane & 31, c4 = 4 * (lane >> 5);
+    auto pack4 = [](float a, float b, float c, float d) {
+      return uint2{uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16),
+                   uint32_t(f32_to_bf16(c)) | (uint32_t(f32_to_bf16(d)) << 16)};
+    };
     if (MODE == EPI_SWIGLU) {
       uint16_t* Hh = static_cast<uint16_t*>(g.out);
 #pragma unroll
       for (int j = 0; j < MW; ++j) {
         const int i = wm + WM * j;
-        if (i >= act_ms) continue;
+        const int row = i * 32 + l32;
+        if (i >= act_ms || row >= ti.rows) continue;
+        uint16_t* hrow = Hh + size_t(ti.row0 + row) * g.ldo + n0;
 #pragma unroll
         for (int f = 0; f < NFG; ++f) {
-          const int col = n0 + fcol[f] + l32;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = i * 32 + acc_row(r, lane);
-            if (row < ti.rows)
-              Hh[size_t(ti.row0 + row) * g.ldo + col] = f32_to_bf16(silu_f32(acc16[j][f][r]) * acc16[j][f + NFG][r]);
+          for (int q = 0; q < 4; ++q) {
+            float h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = silu_f32(acc16[j][f][4 * q + e]) * acc16[j][f + NFG][4 * q + e];
+            *reinterpret_cast<uint2*>(hrow + fcol[f] + 8 * q + c4) = pack4(h[0], h[1], h[2], h[3]);
           }
         }
       }
@@ -477,18 +485,21 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         if (n0 + fcol[f] >= g.N) continue;            // partial column tile (g.N % 128 == 0)
-        const int col = n0 + fcol[f] + l32;
 #pragma unroll
         for (int j = 0; j < MW; ++j) {
           const int i = wm + WM * j;
-          if (i >= act_ms) continue;
+          const int row = i * 32 + l32;
+          if (i >= act_ms || row >= ti.rows) continue;
+          const size_t o = size_t(ti.row0 + row) * g.ldo + n0 + fcol[f] + c4;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = i * 32 + acc_row(r, lane);
-            if (row >= ti.rows) continue;
-            const size_t o = size_t(ti.row0 + row) * g.ldo + col;
-            if (g.out_f32) static_cast<float*>(g.out)[o] = acc16[j][f][r];
-            else static_cast<uint16_t*>(g.out)[o] = f32_to_bf16(acc16[j][f][r]);
+          for (int q = 0; q < 4; ++q) {
+            const f32x16& a = acc16[j][f];
+            if (g.out_f32)
+              *reinterpret_cast<float4*>(static_cast<float*>(g.out) + o + 8 * q) =
+                  float4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+            else
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.out) + o + 8 * q) =
+                  pack4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
           }
         }
       }
