@@ -235,13 +235,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
           for (int s = 0; s < 2; ++s)
             a[s] = rs_cat(*reinterpret_cast<const uint4*>(Ab + rs_swz(ar, 4 * half + 2 * s)),
                           *reinterpret_cast<const uint4*>(Ab + rs_swz(ar, 4 * half + 2 * s + 1)));
-          float ra[16];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint4 v = *reinterpret_cast<const uint4*>(&Sa[buf][i * 32 + 8 * q + 4 * half]);
-            ra[4 * q] = __uint_as_float(v.x); ra[4 * q + 1] = __uint_as_float(v.y);
-            ra[4 * q + 2] = __uint_as_float(v.z); ra[4 * q + 3] = __uint_as_float(v.w);
-          }
+          const float ra = __uint_as_float(Sa[buf][ar]);   // this lane's token row
 #pragma unroll
           for (int f = 0; f < 2; ++f) {
             f32x16 part;
@@ -250,10 +244,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
 #pragma unroll
             for (int s = 0; s < 2; ++s)
               part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  a[s], rs_cat(breg[buf][f][2 * s], breg[buf][f][2 * s + 1]), part, 0, 0, 0, 127, 0, 127);
-            const float sbf = f ? sb1 : sb0;
+                  rs_cat(breg[buf][f][2 * s], breg[buf][f][2 * s + 1]), a[s], part, 0, 0, 0, 127, 0, 127);
+            const float rs = ra * (f ? sb1 : sb0);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][f][r] += part[r] * (ra[r] * sbf);
+            for (int r = 0; r < 16; ++r) acc[i][f][r] = fmaf(part[r], rs, acc[i][f][r]);
           }
         }
       } else {  // MX
@@ -273,8 +267,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
             for (int f = 0; f < 2; ++f) {
               const uint4 bw = breg[buf][f][s];
               const i32x8 b = i32x8{int(bw.x), int(bw.y), int(bw.z), int(bw.w), 0, 0, 0, 0};
-              acc[i][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][f], 0, 4, 0, sa, 0,
-                                                                          int((sbm[buf][f] >> sh) & 0xffu));
+              acc[i][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  b, a, acc[i][f], 4, 0, 0, int((sbm[buf][f] >> sh) & 0xffu), 0, sa);
             }
           }
         }
@@ -282,11 +276,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     }
   }
 
-  // ---- epilogues
+  // ---- epilogues.  bf16: lane l, register r of row block i holds token row
+  // i*32 + acc_row(r, l) and column l & 31 of the fragment (measured faster for
+  // decode).  fp8 and MX: the weight fragment is the MFMA's first operand, so lane
+  // l, register r = 4q + e holds token row i*32 + (l & 31) and column
+  // 8q + 4*(l>>5) + e, and each lane stores runs of four columns.
+  auto pack_bf16 = [](float a, float b, float c, float d) {
+    return uint2{uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16),
+                 uint32_t(f32_to_bf16(c)) | (uint32_t(f32_to_bf16(d)) << 16)};
+  };
   if (MODE == EPI_SWIGLU) {
-    const int col = n0 + wave * 32 + l32;
+    const int c0 = n0 + wave * 32 + 4 * half;      // h column of register 0
     if (BF16) {
       uint16_t* Hh = static_cast<uint16_t*>(g.out);
+      const int col = n0 + wave * 32 + l32;
 #pragma unroll
       for (int i = 0; i < MS; ++i) {
         if (i >= act_ms) continue;
@@ -301,17 +304,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
 #pragma unroll
       for (int i = 0; i < MS; ++i) {
         if (i >= act_ms) continue;
+        float hv[16], m = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float hv = silu_f32(acc[i][0][r]) * acc[i][1][r];
-          const float amax = max_over_lanes32(fabsf(hv));
-          const int row = i * 32 + acc_row(r, lane);
-          const int e = mx_exponent_e4m3(amax);
-          if (row < ti.rows) {
-            Hq[size_t(ti.row0 + row) * g.ldo + col] = uint8_t(f32_to_e4m3(hv * exp2i(-e)));
-            if (l32 == 0)
-              static_cast<uint8_t*>(g.out_scale)[size_t(ti.row0 + row) * (g.N / 32) + col / 32] = uint8_t(e + 127);
+          hv[r] = silu_f32(acc[i][0][r]) * acc[i][1][r];
+          m = fmaxf(m, fabsf(hv[r]));
+        }
+        m = fmaxf(m, __shfl_xor(m, 32, 64));       // the row's other 16 columns
+        const int e = mx_exponent_e4m3(m);
+        const float inv = exp2i(-e);
+        const int row = i * 32 + l32;
+        if (row < ti.rows) {
+          uint8_t* hrow = Hq + size_t(ti.row0 + row) * g.ldo + c0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint32_t packed = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) packed |= f32_to_e4m3(hv[4 * q + k] * inv) << (8 * k);
+            *reinterpret_cast<uint32_t*>(hrow + 8 * q) = packed;
           }
+          if (half == 0)
+            static_cast<uint8_t*>(g.out_scale)[size_t(ti.row0 + row) * (g.N / 32) + (n0 + wave * 32) / 32] =
+                uint8_t(e + 127);
         }
       }
     } else {                                       // fp8 per (row, 128 columns): across the four waves
@@ -319,29 +333,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
 #pragma unroll
       for (int i = 0; i < MS; ++i) {
         if (i >= act_ms) continue;                 // uniform across the block
-        float hv[16];
+        float hv[16], m = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           hv[r] = silu_f32(acc[i][0][r]) * acc[i][1][r];
-          const float m = max_over_lanes32(fabsf(hv[r]));
-          if (l32 == 0) amax_lds[wave][i * 32 + acc_row(r, lane)] = m;
+          m = fmaxf(m, fabsf(hv[r]));
         }
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        const int row = i * 32 + l32;
+        if (half == 0) amax_lds[wave][row] = m;
         __syncthreads();
+        const float amax = fmaxf(fmaxf(amax_lds[0][row], amax_lds[1][row]), fmaxf(amax_lds[2][row], amax_lds[3][row]));
+        const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+        if (row < ti.rows) {
+          uint8_t* hrow = Hq + size_t(ti.row0 + row) * g.ldo + c0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = i * 32 + acc_row(r, lane);
-          const float amax = fmaxf(fmaxf(amax_lds[0][row], amax_lds[1][row]), fmaxf(amax_lds[2][row], amax_lds[3][row]));
-          const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-          if (row < ti.rows) {
-            Hq[size_t(ti.row0 + row) * g.ldo + col] = uint8_t(f32_to_e4m3(hv[r] / s));
-            if (wave == 0 && l32 == 0)
-              static_cast<float*>(g.out_scale)[size_t(ti.row0 + row) * (g.N / 128) + n0 / 128] = s;
+          for (int q = 0; q < 4; ++q) {
+            uint32_t packed = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) packed |= f32_to_e4m3(hv[4 * q + k] / sc) << (8 * k);
+            *reinterpret_cast<uint32_t*>(hrow + 8 * q) = packed;
           }
+          if (wave == 0 && half == 0)
+            static_cast<float*>(g.out_scale)[size_t(ti.row0 + row) * (g.N / 128) + n0 / 128] = sc;
         }
         __syncthreads();
       }
     }
-  } else {
+  } else if (BF16) {
     if (!wave_on) return;
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
@@ -356,6 +375,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
           const size_t o = size_t(ti.row0 + row) * g.ldo + col;
           if (g.out_f32) static_cast<float*>(g.out)[blockIdx.z * g.split_stride + o] = acc[i][f][r];
           else static_cast<uint16_t*>(g.out)[o] = f32_to_bf16(acc[i][f][r]);
+        }
+      }
+    }
+  } else {
+    if (!wave_on) return;
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const int c0 = n0 + wave * 64 + f * 32 + 4 * half;
+#pragma unroll
+      for (int i = 0; i < MS; ++i) {
+        const int row = i * 32 + l32;
+        if (i >= act_ms || row >= ti.rows) continue;
+        const size_t o = size_t(ti.row0 + row) * g.ldo + c0;
+        const f32x16& a = acc[i][f];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (g.out_f32)
+            *reinterpret_cast<float4*>(static_cast<float*>(g.out) + blockIdx.z * g.split_stride + o + 8 * q) =
+                float4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+          else
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.out) + o + 8 * q) =
+                pack_bf16(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
         }
       }
     }
@@ -374,7 +415,7 @@ static void rs_launch(int ms, dim3 grid, const GemmArgs& g, hipStream_t st) {
     }
   }
   if (ms <= 1) ffn_rs_kernel<1, MODE, RECIPE, RS_NST1><<<grid, 256, 0, st>>>(g);
-  else ffn_rs_kernel<2, MODE, RECIPE, RS_NST2><<<grid, 256, 0, st>>>(g);
+  else ffn_rs_kernel<2, MODE, RECIPE, RS_NST2, (RECIPE == MOE_RECIPE_FP8_B128 ? 2 : 1)><<<grid, 256, 0, st>>>(g);
 }
 
 template <int MODE>
