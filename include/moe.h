@@ -90,7 +90,12 @@ typedef enum {
  *   n_group > 1 needs at least 2 experts per group;
  *   topk_group * num_experts / n_group >= top_k;
  *   recipes other than F32 need hidden, intermediate and shared_intermediate
- *   to be multiples of 128; F32 needs multiples of 32. */
+ *   to be multiples of 128; F32 needs multiples of 32;
+ *   swiglu_limit finite and >= 0.
+ * swiglu_limit (the optional SwiGLU truncation of the DeepSeek-V4-Pro overview,
+ * FFN entry; the pages give only its name): when > 0, every SwiGLU (routed and
+ * shared experts) computes SiLU(min(g, L)) * clamp(u, -L, L) with L the limit,
+ * g = W1 x and u = W3 x. */
 typedef struct {
   int32_t num_tokens;            /* T */
   int32_t hidden;                /* H */
@@ -105,6 +110,7 @@ typedef struct {
   int32_t norm_topk_prob;        /* 1: weights normalised to sum 1 before scaling */
   float routed_scaling_factor;   /* 2.827 in the walk-through; route_scale 2.5 in V4-Pro */
   int32_t recipe;                /* moe_recipe_t */
+  float swiglu_limit;            /* > 0: SwiGLU clamp, see below; 0: none */
 } moe_config_t;
 
 /* One set of experts, expert-major and contiguous.
@@ -155,7 +161,8 @@ moe_status_t moe_permute(const moe_config_t* cfg, const int32_t* topk_idx, const
                          void* stream);
 
 /* moe_infer per-expert MLP (walk-through section 3.4): for every expert e and
- * row p in its block, y_perm[p] = W2_e (SiLU(W1_e x) * (W3_e x)) with x =
+ * row p in its block, y_perm[p] = W2_e (SiLU(W1_e x) * (W3_e x)) (clamped as
+ * swiglu_limit says) with x =
  * x_perm[p] (dequantised by its scales).  For FP8_B128 and MXFP4 the SwiGLU
  * output is re-quantised to the activation format before the down projection.
  * fp32 accumulation.  y_perm [T*k][H] (fp32 for F32, else bf16). */

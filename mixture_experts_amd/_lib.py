@@ -24,7 +24,8 @@ class MoeConfig(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("intermediate", ctypes.c_int32), ("num_shared", ctypes.c_int32),
                 ("shared_intermediate", ctypes.c_int32), ("n_group", ctypes.c_int32),
                 ("topk_group", ctypes.c_int32), ("score_func", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32),
-                ("routed_scaling_factor", ctypes.c_float), ("recipe", ctypes.c_int32)]
+                ("routed_scaling_factor", ctypes.c_float), ("recipe", ctypes.c_int32),
+                ("swiglu_limit", ctypes.c_float)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -75,7 +76,8 @@ def make_config(cfg) -> MoeConfig:
     return MoeConfig(int(cfg.num_tokens), int(cfg.hidden), int(cfg.num_experts), int(cfg.top_k),
                      int(cfg.intermediate), int(cfg.num_shared), int(cfg.shared_intermediate), int(cfg.n_group),
                      int(cfg.topk_group), int(cfg.score_func), int(bool(cfg.norm_topk_prob)),
-                     float(cfg.routed_scaling_factor), int(cfg.recipe))
+                     float(cfg.routed_scaling_factor), int(cfg.recipe),
+                     float(getattr(cfg, "swiglu_limit", 0.0)))
 
 
 def _ptr(t):

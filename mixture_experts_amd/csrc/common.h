@@ -105,4 +105,15 @@ __device__ __forceinline__ uint32_t orderable_f32(float f) {
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
 
+// SwiGLU of one (gate, up) pair.  limit > 0 (swiglu_limit, DeepSeek-V4-Pro
+// overview, FFN entry) first clamps the gate to at most the limit and the up
+// projection to [-limit, limit].
+__device__ __forceinline__ float swiglu_f32(float g, float u, float limit) {
+  if (limit > 0.0f) {
+    g = fminf(g, limit);
+    u = fminf(fmaxf(u, -limit), limit);
+  }
+  return silu_f32(g) * u;
+}
+
 }  // namespace moe

@@ -476,7 +476,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
           for (int q = 0; q < 4; ++q) {
             float h[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) h[e] = silu_f32(acc16[j][f][4 * q + e]) * acc16[j][f + NFG][4 * q + e];
+            for (int e = 0; e < 4; ++e) h[e] = swiglu_f32(acc16[j][f][4 * q + e], acc16[j][f + NFG][4 * q + e], g.swiglu_limit);
             *reinterpret_cast<uint2*>(hrow + fcol[f] + 8 * q + c4) = pack4(h[0], h[1], h[2], h[3]);
           }
         }
@@ -524,7 +524,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
         for (int c = 0; c < NC / 2; ++c)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            hv[c][r] = silu_f32(acc4[u][c][r]) * acc4[u][c + NC / 2][r];
+            hv[c][r] = swiglu_f32(acc4[u][c][r], acc4[u][c + NC / 2][r], g.swiglu_limit);
             m = fmaxf(m, fabsf(hv[c][r]));
           }
         m = fmaxf(m, __shfl_xor(m, 16, 64));

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(GemmArgs g) {
       a0 = fmaf(A[k], wg[k], a0);
       a1 = fmaf(A[k], wu[k], a1);
     }
-    static_cast<float*>(g.out)[size_t(ti.row0 + r) * g.ldo + col] = silu_f32(a0) * a1;
+    static_cast<float*>(g.out)[size_t(ti.row0 + r) * g.ldo + col] = swiglu_f32(a0, a1, g.swiglu_limit);
     return;
   }
   float acc = 0.0f;
@@ -172,7 +172,7 @@ hipError_t launch_combine_rows(const moe_config_t& c, const void* y_perm, const 
 // (sub-expert s: gate columns s*2Is .. +Is, up columns s*2Is+Is .. +Is), summed in
 // order; h[t][s*Is + c] = bf16(SiLU(gate) * up).
 __global__ __launch_bounds__(256) void swiglu_slabs(const float* __restrict__ part, int nz, int T, int nes, int Is,
-                                                    uint16_t* __restrict__ h) {
+                                                    float limit, uint16_t* __restrict__ h) {
   const int SI = nes * Is;
   const size_t stride = size_t(T) * 2 * SI;
   const size_t n4 = size_t(T) * SI / 4;
@@ -188,16 +188,17 @@ __global__ __launch_bounds__(256) void swiglu_slabs(const float* __restrict__ pa
       us.x += uv.x; us.y += uv.y; us.z += uv.z; us.w += uv.w;
     }
     uint2 o;
-    o.x = uint32_t(f32_to_bf16(silu_f32(gs.x) * us.x)) | (uint32_t(f32_to_bf16(silu_f32(gs.y) * us.y)) << 16);
-    o.y = uint32_t(f32_to_bf16(silu_f32(gs.z) * us.z)) | (uint32_t(f32_to_bf16(silu_f32(gs.w) * us.w)) << 16);
+    o.x = uint32_t(f32_to_bf16(swiglu_f32(gs.x, us.x, limit))) | (uint32_t(f32_to_bf16(swiglu_f32(gs.y, us.y, limit))) << 16);
+    o.y = uint32_t(f32_to_bf16(swiglu_f32(gs.z, us.z, limit))) | (uint32_t(f32_to_bf16(swiglu_f32(gs.w, us.w, limit))) << 16);
     *reinterpret_cast<uint2*>(h + i) = o;
   }
 }
 
-hipError_t launch_swiglu_slabs(const float* part, int nz, int T, int nes, int Is, uint16_t* h, hipStream_t st) {
+hipError_t launch_swiglu_slabs(const float* part, int nz, int T, int nes, int Is, float limit, uint16_t* h,
+                               hipStream_t st) {
   const size_t n4 = size_t(T) * nes * Is / 4;
   const int blocks = int(std::min<size_t>((n4 + 255) / 256, 2048));
-  swiglu_slabs<<<blocks, 256, 0, st>>>(part, nz, T, nes, Is, h);
+  swiglu_slabs<<<blocks, 256, 0, st>>>(part, nz, T, nes, Is, limit, h);
   return hipGetLastError();
 }
 

@@ -296,7 +296,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = i * 32 + acc_row(r, lane);
-          if (row < ti.rows) Hh[size_t(ti.row0 + row) * g.ldo + col] = f32_to_bf16(silu_f32(acc[i][0][r]) * acc[i][1][r]);
+          if (row < ti.rows) Hh[size_t(ti.row0 + row) * g.ldo + col] = f32_to_bf16(swiglu_f32(acc[i][0][r], acc[i][1][r], g.swiglu_limit));
         }
       }
     } else if (MX) {                               // MXFP8 per (row, 32 columns): one fragment per block
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
         float hv[16], m = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          hv[r] = silu_f32(acc[i][0][r]) * acc[i][1][r];
+          hv[r] = swiglu_f32(acc[i][0][r], acc[i][1][r], g.swiglu_limit);
           m = fmaxf(m, fabsf(hv[r]));
         }
         m = fmaxf(m, __shfl_xor(m, 32, 64));       // the row's other 16 columns
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
         float hv[16], m = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          hv[r] = silu_f32(acc[i][0][r]) * acc[i][1][r];
+          hv[r] = swiglu_f32(acc[i][0][r], acc[i][1][r], g.swiglu_limit);
           m = fmaxf(m, fabsf(hv[r]));
         }
         m = fmaxf(m, __shfl_xor(m, 32, 64));

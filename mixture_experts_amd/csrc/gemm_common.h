@@ -27,6 +27,7 @@ struct GemmArgs {
   void* out_scale;          // h scales for the quantised recipes
   int ldo;
   int out_f32;              // down projection: store fp32 instead of bf16
+  float swiglu_limit;       // SwiGLU epilogue: > 0 clamps gate and up first (swiglu_f32)
   // Fused gather: when a_map is set, the A row (and A-scale row) of pair row p is
   // a_map[p] / a_div -- the token of the p-th sorted (token, slot) pair -- so the
   // GEMM reads the token rows directly instead of a gathered copy.

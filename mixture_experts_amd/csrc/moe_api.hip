@@ -14,7 +14,8 @@ hipError_t launch_rs_down(int recipe, int ms, int m_tiles, const GemmArgs& g, hi
 hipError_t launch_f32(int mode, int m_tiles, const GemmArgs& g, hipStream_t st);
 hipError_t launch_combine_rows(const moe_config_t& c, const void* y_perm, const int32_t* pair_pos,
                                const float* topk_w, const float* sh, int nsh, void* out, hipStream_t st);
-hipError_t launch_swiglu_slabs(const float* part, int nz, int T, int nes, int Is, uint16_t* h, hipStream_t st);
+hipError_t launch_swiglu_slabs(const float* part, int nz, int T, int nes, int Is, float limit, uint16_t* h,
+                               hipStream_t st);
 hipError_t launch_build_tiles2(const int32_t* offsets, int E, int thresh, int bm_large, int bm_small,
                                int32_t* tiles_l, int32_t* tiles_s, hipStream_t st);
 hipError_t launch_lds_swiglu(bool fp8, int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
@@ -35,6 +36,7 @@ bool valid_config(const moe_config_t* c) {
   if (c->recipe < MOE_RECIPE_F32 || c->recipe > MOE_RECIPE_MXFP4) return false;
   if (!(c->routed_scaling_factor == c->routed_scaling_factor)) return false;
   if (int64_t(c->num_tokens) * c->top_k > (int64_t(1) << 30)) return false;
+  if (!(c->swiglu_limit >= 0.0f && c->swiglu_limit <= 3.0e38f)) return false;   // finite, >= 0
   return true;
 }
 
@@ -189,6 +191,7 @@ hipError_t launch_grouped_ffn(const moe_config_t& c, const int32_t* offsets, con
   if (e != hipSuccess) return e;
   const bool fp8 = c.recipe == MOE_RECIPE_FP8_B128;
   GemmArgs g{};
+  g.swiglu_limit = c.swiglu_limit;
   g.A = x_perm;
   g.A_scale = x_perm_scale;
   g.a_map = a_map;
@@ -277,7 +280,7 @@ hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32
       ProfScope p(MOE_K_SHARED_GATE_UP, st);
       e = launch_rs_down(MOE_RECIPE_BF16, ss.ms, ss.mt, g, st, ss.ks1);
       if (e == hipSuccess)
-        e = launch_swiglu_slabs(sh_part, ss.ks1, T, c.num_shared, c.shared_intermediate,
+        e = launch_swiglu_slabs(sh_part, ss.ks1, T, c.num_shared, c.shared_intermediate, c.swiglu_limit,
                                 static_cast<uint16_t*>(h_shared), st);
     }
     if (e != hipSuccess) return e;
@@ -307,6 +310,7 @@ hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32
   const int ms = lds ? (T >= 256 ? 8 : 4) : shared_ms(T);
   const int BM = f32 ? 16 : ms * 32, mt = (T + BM - 1) / BM;
   GemmArgs g{};
+  g.swiglu_limit = c.swiglu_limit;
   g.A = x;
   g.lda = c.hidden;
   g.dense_rows = T;

@@ -314,13 +314,23 @@ def silu(z: np.ndarray) -> np.ndarray:
     return z * sig
 
 
+def swiglu(g: np.ndarray, u: np.ndarray, limit: float = 0.0) -> np.ndarray:
+    """SiLU(g) * u.  With swiglu_limit > 0 (V4-Pro overview, FFN entry: an optional
+    truncation of the SwiGLU), the gate is first clamped to at most the limit and the
+    up projection to [-limit, limit] (reading: the pages give only the name)."""
+    if limit > 0:
+        g = np.minimum(g, limit)
+        u = np.clip(u, -limit, limit)
+    return silu(g) * u
+
+
 def expert_mlp(x64: np.ndarray, w13: np.ndarray, w2: np.ndarray, recipe: int = RECIPE_F32,
-               quantize_h: bool = False) -> np.ndarray:
+               quantize_h: bool = False, limit: float = 0.0) -> np.ndarray:
     """DeepseekV3MLP on a block of rows: down(SiLU(gate(x)) * up(x)); fp64."""
     I = w13.shape[0] // 2
     g = x64 @ w13[:I].T
     u = x64 @ w13[I:].T
-    h = silu(g) * u
+    h = swiglu(g, u, limit)
     if quantize_h:
         h = quantize_rows(recipe, h.astype(F32))
     return h @ w2.T
@@ -340,6 +350,7 @@ def moe_forward(cfg, x64: np.ndarray, gate_w64: np.ndarray, bias32: np.ndarray,
     I = cfg.intermediate
     recipe = cfg.recipe
     quant = recipe in (RECIPE_FP8_B128, RECIPE_MXFP4)
+    limit = float(getattr(cfg, "swiglu_limit", 0.0))
     if routing is None:
         routing = route(cfg, x64, gate_w64, bias32)
     if perm is None:
@@ -356,11 +367,11 @@ def moe_forward(cfg, x64: np.ndarray, gate_w64: np.ndarray, bias32: np.ndarray,
     for e in np.unique(idx):
         rows, slots = np.nonzero(idx == e)
         w13, w2 = dequant_expert(recipe, expert_raw(int(e)), I, H)
-        y[rows, slots] = expert_mlp(xq[rows], w13, w2, recipe, quantize_h=quant)
+        y[rows, slots] = expert_mlp(xq[rows], w13, w2, recipe, quantize_h=quant, limit=limit)
     routed = np.einsum("nk,nkh->nh", w, y)
     shared = np.zeros_like(routed)
     for s in range(shared_w13.shape[0]):
-        shared += expert_mlp(xa, shared_w13[s], shared_w2[s])
+        shared += expert_mlp(xa, shared_w13[s], shared_w2[s], limit=limit)
     return dict(out=routed + shared, y=y, routed=routed, shared=shared, routing=routing,
                 perm=perm, tokens=tokens)
 

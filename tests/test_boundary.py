@@ -29,8 +29,8 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_config_struct_matches_header_layout():
-    # 12 int32 + 1 float, no padding
-    assert ctypes.sizeof(M.MoeConfig) == 13 * 4
+    # 12 int32 + 2 float, no padding
+    assert ctypes.sizeof(M.MoeConfig) == 14 * 4
     assert ctypes.sizeof(M.MoeWeights) == 4 * ctypes.sizeof(ctypes.c_void_p)
 
 
@@ -58,6 +58,9 @@ BAD = [
     dict(num_experts=2000, top_k=4),
     dict(score_func=7),
     dict(recipe=9),
+    dict(swiglu_limit=-1.0),
+    dict(swiglu_limit=float("nan")),
+    dict(swiglu_limit=float("inf")),
 ]
 
 

@@ -5,6 +5,8 @@ bit-exact, quantised activation bytes bit-exact, outputs within the recipe's
 relative-L2 tolerance).  Full-size workloads, in the launch configuration the
 benchmark times (moe_forward): all routing indices bit-exact, the permutation
 bit-exact, and the outputs of sampled tokens within tolerance."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -78,6 +80,45 @@ def test_runs_are_bit_identical(cfg):
     out1 = a.out.clone()
     HN.run_forward(inp, a)
     assert torch.equal(out1, a.out)
+
+
+# Method variants (norm_topk_prob = false; swiglu_limit > 0) on workloads that
+# between them take every SwiGLU epilogue: register-streaming bf16/fp8/MX tiles,
+# LDS-staged bf16/fp8 tiles, the fp32 kernel and the decode shared expert's
+# K-split slabs.  The limit clips a large share of the gate and up values
+# (their standard deviation is about 0.4 at these sizes).
+VARIANTS = [
+    (C.MINI_GROUPED_BF16, dict(swiglu_limit=0.25)),
+    (C.MINI_DECODE_BF16, dict(swiglu_limit=0.25)),
+    (C.MINI_MIXED_BF16, dict(swiglu_limit=0.25)),
+    (C.MINI_FP8, dict(swiglu_limit=0.25)),
+    (C.MINI_MXFP4, dict(swiglu_limit=0.25)),
+    (C.MINI_MXFP4_WIDE, dict(swiglu_limit=0.25)),
+    (C.MINI_F32, dict(swiglu_limit=0.2)),
+    (C.MINI_GROUPED_BF16, dict(norm_topk_prob=False)),
+    (C.MINI_FP8, dict(norm_topk_prob=False)),
+    (C.TINY_F32, dict(norm_topk_prob=False, swiglu_limit=0.2)),
+]
+
+
+@pytest.mark.parametrize("case", VARIANTS,
+                         ids=lambda c: c[0].name + "-" + ",".join(f"{k}={v}" for k, v in c[1].items()))
+def test_method_variants(case):
+    base, kw = case
+    cfg = base.replace(**kw)
+    inp = G.generate(cfg, device="cuda")             # same tensors as the base workload (same name)
+    b = HN.run_stages(inp)
+    ref = HN.oracle(inp)
+    _check_routing(b, ref)
+    _check_permutation(b, ref)
+    tol = HN.TOL[cfg.recipe]
+    err = HN.rel_l2(HN.out_f64(b.out), ref["out"])
+    assert err < tol, f"out rel-L2 {err:.3e}"
+    b2 = HN.run_forward(inp)
+    assert torch.equal(b2.out, b.out)
+    # the variant changes the result well beyond the tolerance
+    ref0 = HN.oracle(dataclasses.replace(inp, cfg=base))
+    assert HN.rel_l2(ref["out"], ref0["out"]) > 5 * tol
 
 
 def _edge_inputs(kind):

@@ -235,6 +235,77 @@ def test_expert_mlp_matches_scalar_loops():
     np.testing.assert_allclose(O.expert_mlp(x, w13, w2), _loops_mlp(x, w13, w2), rtol=1e-12, atol=1e-12)
 
 
+# ------------------------------------------------------------------ method variants
+def test_unnormalised_weights_are_the_scaled_scores_of_the_picks():
+    """norm_topk_prob = false (walk-through 3.3 normalises only when the flag is set):
+    the weights keep the ratios of the normalised ones and sum to scale * (sum of
+    the picked scores), each in (0, scale) for sigmoid scores."""
+    rng = np.random.default_rng(11)
+    cfg = rand_small_cfg(num_experts=32, top_k=8, routed_scaling_factor=2.827)
+    x = rng.standard_normal((60, 64)); wg = rng.standard_normal((32, 64)) / 8
+    b = rng.normal(0, 0.01, 32).astype(F32)
+    rn = O.route(cfg, x, wg, b)
+    ru = O.route(cfg.replace(norm_topk_prob=False), x, wg, b)
+    assert np.array_equal(rn["idx"], ru["idx"])                      # selection does not depend on it
+    wn, wu = rn["w"].astype(np.float64), ru["w"].astype(np.float64)
+    assert np.all((wu > 0) & (wu < 2.827))
+    ssum = wu.sum(axis=1, keepdims=True) / 2.827                      # sum of the picked scores
+    np.testing.assert_allclose(wn * ssum, wu, rtol=1e-6)
+    assert np.all(np.abs(ssum - 1.0) > 1e-3)                          # the two variants differ
+
+
+def test_swiglu_limit_zero_or_huge_is_plain_swiglu():
+    rng = np.random.default_rng(12)
+    g, u = rng.standard_normal((2, 500)) * 3
+    plain = O.silu(g) * u
+    assert np.array_equal(O.swiglu(g, u, 0.0), plain)
+    assert np.array_equal(O.swiglu(g, u, 1e30), plain)
+
+
+def test_swiglu_limit_saturates_as_read():
+    """The reading of the optional truncation: gate clamped from above only, up
+    clamped on both sides, SiLU applied after."""
+    L = 1.0
+    silu_L = 1.0 / (1.0 + math.exp(-1.0))                             # SiLU(1)
+    u = np.array([-3.0, -0.5, 0.0, 0.7, 5.0])
+    # gate above the limit: SiLU(L) * clamp(u)
+    np.testing.assert_allclose(O.swiglu(np.full(5, 7.0), u, L), silu_L * np.array([-1.0, -0.5, 0.0, 0.7, 1.0]),
+                               rtol=1e-15)
+    # gate far below -L is not raised to -L: SiLU(-10) * u, not SiLU(-1) * u
+    silu_m10 = -10.0 / (1.0 + math.exp(10.0))
+    np.testing.assert_allclose(O.swiglu(np.full(5, -10.0), u, L), silu_m10 * np.clip(u, -1, 1), rtol=1e-12)
+    # inside the box nothing changes
+    gi = np.array([-0.9, -0.2, 0.3, 0.99, 1.0])
+    ui = np.array([0.5, -1.0, 1.0, -0.3, 0.2])
+    np.testing.assert_allclose(O.swiglu(gi, ui, L), gi / (1 + np.exp(-gi)) * ui, rtol=1e-15)
+    # bounded output: |h| <= L * max(SiLU(L), -min SiLU) for any input
+    rng = np.random.default_rng(13)
+    g, uu = rng.standard_normal((2, 10000)) * 20
+    assert np.all(np.abs(O.swiglu(g, uu, L)) <= L * max(silu_L, 0.27846454) + 1e-12)
+
+
+def test_swiglu_limit_in_the_expert_mlp_matches_scalar_loops():
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((3, 8)); w13 = rng.standard_normal((8, 8)); w2 = rng.standard_normal((8, 4))
+    L = 0.8
+    I = 4
+    want = []
+    for row in x:
+        h = []
+        for i in range(I):
+            g = sum(a * b for a, b in zip(row, w13[i]))
+            u = sum(a * b for a, b in zip(row, w13[I + i]))
+            if g > L:
+                g = L
+            if u > L:
+                u = L
+            elif u < -L:
+                u = -L
+            h.append(g / (1 + math.exp(-g)) * u)
+        want.append([sum(a * b for a, b in zip(h, w2[n])) for n in range(len(w2))])
+    np.testing.assert_allclose(O.expert_mlp(x, w13, w2, limit=L), np.array(want), rtol=1e-12, atol=1e-12)
+
+
 def _f32_raw(w13, w2):
     return lambda e: {"w13": w13[e], "w2": w2[e]}
 

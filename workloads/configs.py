@@ -45,6 +45,7 @@ class MoEConfig:
     norm_topk_prob: bool = True
     routed_scaling_factor: float = 2.827
     recipe: int = RECIPE_BF16
+    swiglu_limit: float = 0.0   # > 0: gate clamped to <= limit, up to [-limit, limit] before SiLU(g)*u
     # --- synthetic-input recipe (not layer hyper-parameters) ---
     seed: int = 0
     gate_std: float = 0.02
