@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--config", default="decode_bf16")
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--residual", action="store_true",
+                    help="time the residual form instead: out = h + MoE(RMSNorm(h)) (moe_forward_residual)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size reference for HBM counters)")
     return ap.parse_args()
@@ -138,7 +140,11 @@ def main():
     print(f"[bench] {cfg.name}: inputs ready in {time.time() - t_gen:.1f} s", file=sys.stderr, flush=True)
 
     def step():
-        M.moe_forward(mcfg, inp.x, inp.gate_w, inp.bias, ex, sh, b.out, b.topk_idx, b.topk_w, b.ws)
+        if args.residual:
+            M.moe_forward_residual(mcfg, inp.x, inp.norm_w, G.RMS_EPS, inp.gate_w, inp.bias, ex, sh, b.out,
+                                   b.topk_idx, b.topk_w, b.ws)
+        else:
+            M.moe_forward(mcfg, inp.x, inp.gate_w, inp.bias, ex, sh, b.out, b.topk_idx, b.topk_w, b.ws)
 
     if args.copy_calibration_mib:
         src = torch.ones(args.copy_calibration_mib << 18, dtype=torch.float32, device="cuda")
@@ -197,7 +203,8 @@ def main():
                    "top_k": cfg.top_k, "I": cfg.intermediate, "shared": cfg.num_shared,
                    "shared_I": cfg.shared_intermediate, "n_group": cfg.n_group, "topk_group": cfg.topk_group,
                    "recipe": C.RECIPE_NAMES[cfg.recipe], "touched_experts": touched,
-                   "max_expert_rows": int(counts.max()), "parallelism": "single GPU"},
+                   "max_expert_rows": int(counts.max()), "parallelism": "single GPU",
+                   "form": "residual (h + MoE(RMSNorm(h)))" if args.residual else "moe"},
         "roofline": roof,
         "kernels_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in prof.items() if v[1]},
         "wall_s": round(wall, 3),
@@ -206,6 +213,8 @@ def main():
         n = args.cpu_sample or {"tiny_fp32": 64, "decode_bf16": 6, "prefill_bf16_grouped": 6,
                                 "finegrained_mxfp4": 4, "skewed_fp8": 6}.get(cfg.name, 8)
         line["cpu_baseline"] = cpu_baseline(cfg, inp, n)
+        if args.residual:
+            line["cpu_baseline"]["sample"] += " (MoE part of the residual form)"
     print(json.dumps(line), flush=True)
 
 

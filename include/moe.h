@@ -16,13 +16,19 @@
  *   moe_combine      - moe_infer's put-back x top-k weight sum, plus the
  *                      always-on shared expert(s) of DeepseekV3MoE.forward
  *                      (section 3.4);
- *   moe_forward      - all of the above in one call.
+ *   moe_forward      - all of the above in one call;
+ *   moe_rmsnorm, moe_forward_residual - the decoder layer around the MoE
+ *                      (section 3.5): post_attention_layernorm in front, the
+ *                      residual added in the combine.
  *
  * Conventions for every entry point
  *   - Every buffer pointer is a DEVICE pointer owned by the caller; the library
  *     never allocates, frees or copies to the host, and never synchronises.
  *     Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
- *   - Inputs are never written.  Outputs are fully overwritten.
+ *   - Inputs are never written (except an `out` that the caller makes the same
+ *     buffer as `resid`).  Outputs are fully overwritten.
+ *   - Tensor pointers are 16-byte aligned (rows are read in 16-byte pieces);
+ *     moe_rmsnorm and moe_forward_residual check this for their tensors.
  *   - `ws` is caller-owned device scratch of at least moe_workspace_bytes(cfg)
  *     bytes, 256-byte aligned.  Two calls that run at the same time need
  *     distinct workspaces.
@@ -188,6 +194,28 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* ga
                          const moe_weights_t* shared, void* out, int32_t* topk_idx_out,
                          float* topk_w_out, void* ws, size_t ws_bytes, void* stream);
 
+/* post_attention_layernorm (walk-through section 3.5; RMSNorm kept in fp32 in
+ * the V4-Pro overview): for each token row t of the residual stream resid [T][H]
+ * (fp32 for F32, else bf16),
+ *   x[t][i] = act( fp32( (resid[t][i] * r) * norm_w[i] ) ),
+ *   r = 1 / sqrt( sum_i resid[t][i]^2 / H + eps ),
+ * with the sum, the root and both products in fp64 and act the activation format
+ * (fp32, or bf16 rounded to nearest even).  norm_w [H] fp32.  x [T][H] must not
+ * overlap resid.  Needs no workspace; eps must be finite and >= 0. */
+moe_status_t moe_rmsnorm(const moe_config_t* cfg, const void* resid, const float* norm_w, float eps,
+                         void* x, void* stream);
+
+/* The MoE half of a decoder layer (walk-through section 3.5) in one call:
+ *   out = resid + DeepseekV3MoE( moe_rmsnorm(resid) ),
+ * the residual added in fp32 inside the combine before its single rounding.
+ * out may be the same buffer as resid (every element is read before it is
+ * written, by the same thread).  The normalised rows live in the workspace. */
+moe_status_t moe_forward_residual(const moe_config_t* cfg, const void* resid, const float* norm_w,
+                                  float eps, const float* gate_w, const float* bias,
+                                  const moe_weights_t* experts, const moe_weights_t* shared,
+                                  void* out, int32_t* topk_idx_out, float* topk_w_out, void* ws,
+                                  size_t ws_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* moe_status_string(moe_status_t status);
 
@@ -210,6 +238,7 @@ typedef enum {
   MOE_K_SHARED_GATE_UP,        /* shared expert(s) gate/up + SwiGLU                   */
   MOE_K_SHARED_DOWN_COMBINE,   /* shared down projection (fp32 recipe: + put-back sum) */
   MOE_K_COMBINE,               /* weighted put-back sum (+ shared-expert rows)        */
+  MOE_K_RMSNORM,               /* post_attention_layernorm (moe_rmsnorm, residual form) */
   MOE_K_COUNT
 } moe_kernel_tag_t;
 

@@ -14,9 +14,10 @@ RECIPE_F32, RECIPE_BF16, RECIPE_FP8_B128, RECIPE_MXFP4 = range(4)
 SCORE_SIGMOID, SCORE_SQRTSOFTPLUS = range(2)
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
-           "moe_forward", "moe_status_string", "moe_profile_start", "moe_profile_stop", "moe_kernel_tag_name")
+           "moe_forward", "moe_rmsnorm", "moe_forward_residual", "moe_status_string", "moe_profile_start",
+           "moe_profile_stop", "moe_kernel_tag_name")
 KERNEL_TAGS = ("gate_logits", "router", "perm_hist", "perm_scan", "perm_scatter", "gather", "tile_list",
-               "ffn_gate_up", "ffn_down", "shared_gate_up", "shared_down_combine", "combine")
+               "ffn_gate_up", "ffn_down", "shared_gate_up", "shared_down_combine", "combine", "rmsnorm")
 
 
 class MoeConfig(ctypes.Structure):
@@ -60,12 +61,14 @@ def load() -> ctypes.CDLL:
     lib.moe_grouped_ffn.argtypes = [cfgp, vp, vp, vp, wp, vp, vp, sz, vp]
     lib.moe_combine.argtypes = [cfgp, vp, vp, vp, vp, wp, vp, vp, sz, vp]
     lib.moe_forward.argtypes = [cfgp, vp, vp, vp, wp, wp, vp, vp, vp, vp, sz, vp]
+    lib.moe_rmsnorm.argtypes = [cfgp, vp, vp, ctypes.c_float, vp, vp]
+    lib.moe_forward_residual.argtypes = [cfgp, vp, vp, ctypes.c_float, vp, vp, wp, wp, vp, vp, vp, vp, sz, vp]
     lib.moe_profile_start.argtypes = [ctypes.c_int32]
     lib.moe_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), ctypes.c_int32]
     lib.moe_kernel_tag_name.argtypes = [ctypes.c_int32]
     lib.moe_kernel_tag_name.restype = ctypes.c_char_p
-    for name in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_profile_start",
-                 "moe_profile_stop"):
+    for name in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_rmsnorm",
+                 "moe_forward_residual", "moe_profile_start", "moe_profile_stop"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -134,6 +137,20 @@ def moe_forward(cfg, x, gate_w, bias, experts: MoeWeights, shared: MoeWeights | 
                               ctypes.byref(shared) if shared is not None else None, _ptr(out), _ptr(topk_idx_out),
                               _ptr(topk_w_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "moe_forward")
+
+
+def moe_rmsnorm(cfg, resid, norm_w, eps: float, x, stream=None):
+    _check(load().moe_rmsnorm(ctypes.byref(cfg), _ptr(resid), _ptr(norm_w), float(eps), _ptr(x), _stream(stream)),
+           "moe_rmsnorm")
+
+
+def moe_forward_residual(cfg, resid, norm_w, eps: float, gate_w, bias, experts: MoeWeights,
+                         shared: MoeWeights | None, out, topk_idx_out, topk_w_out, ws, stream=None):
+    _check(load().moe_forward_residual(ctypes.byref(cfg), _ptr(resid), _ptr(norm_w), float(eps), _ptr(gate_w),
+                                       _ptr(bias), ctypes.byref(experts),
+                                       ctypes.byref(shared) if shared is not None else None, _ptr(out),
+                                       _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(ws), ws.numel() * ws.element_size(),
+                                       _stream(stream)), "moe_forward_residual")
 
 
 def moe_profile_start(max_launches: int = 4096):

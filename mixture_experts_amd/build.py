@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
-SOURCES = ["moe_api.hip", "route.hip", "permute.hip", "ffn_rs.hip", "ffn_misc.hip", "ffn_lds.hip"]
+SOURCES = ["moe_api.hip", "route.hip", "permute.hip", "ffn_rs.hip", "ffn_misc.hip", "ffn_lds.hip", "norm.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

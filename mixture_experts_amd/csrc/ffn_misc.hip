@@ -85,6 +85,7 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(GemmArgs g) {
   } else {
     const int t = ti.row0 + r, k = g.topk;
     const float* Yp = static_cast<const float*>(g.y_perm);
+    if (g.resid) acc += static_cast<const float*>(g.resid)[size_t(t) * g.ldo + col];
     for (int j = 0; j < k; ++j)
       acc += g.topk_w[size_t(t) * k + j] * Yp[size_t(g.pair_pos[size_t(t) * k + j]) * g.ldo + col];
     static_cast<float*>(g.out)[size_t(t) * g.ldo + col] = acc;
@@ -106,9 +107,12 @@ hipError_t launch_f32(int mode, int m_tiles, const GemmArgs& g, hipStream_t st) 
 // ---------------------------------------------------------------------------
 // sh: nsh fp32 slabs [T][H], sh_stride elements apart, summed in order (K-split
 // partial products of the shared expert's down projection; nsh = 1: its rows).
+// resid (nullable): bf16 residual rows [T][H], added first.  out may alias resid:
+// each thread reads its 8 channels of resid before writing them.
 __global__ __launch_bounds__(256) void combine_bf16(const uint16_t* __restrict__ yp, const int32_t* __restrict__ pair_pos,
                                                     const float* __restrict__ w, const float* __restrict__ sh, int nsh,
-                                                    size_t sh_stride, int k, int H, uint16_t* __restrict__ out) {
+                                                    size_t sh_stride, int k, int H, const uint16_t* resid,
+                                                    uint16_t* out) {
   __shared__ int32_t pos[16];
   __shared__ float wt[16];
   const int t = blockIdx.x;
@@ -121,6 +125,15 @@ __global__ __launch_bounds__(256) void combine_bf16(const uint16_t* __restrict__
     float acc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+    if (resid) {
+      const uint4 v = reinterpret_cast<const uint4*>(resid + size_t(t) * H)[c];
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = __uint_as_float(u[q] << 16);
+        acc[2 * q + 1] = __uint_as_float(u[q] & 0xffff0000u);
+      }
+    }
     for (int z = 0; z < nsh; ++z) {
       const float4* src = reinterpret_cast<const float4*>(sh + z * sh_stride + size_t(t) * H);
       const float4 a = src[2 * c], b = src[2 * c + 1];
@@ -146,10 +159,11 @@ __global__ __launch_bounds__(256) void combine_bf16(const uint16_t* __restrict__
 }
 
 __global__ __launch_bounds__(256) void combine_f32(const float* __restrict__ yp, const int32_t* __restrict__ pair_pos,
-                                                   const float* __restrict__ w, int k, int H, float* __restrict__ out) {
+                                                   const float* __restrict__ w, int k, int H, const float* resid,
+                                                   float* out) {
   const int t = blockIdx.x;
   for (int n = threadIdx.x; n < H; n += 256) {
-    float acc = 0.0f;
+    float acc = resid ? resid[size_t(t) * H + n] : 0.0f;
     for (int j = 0; j < k; ++j) acc += w[size_t(t) * k + j] * yp[size_t(pair_pos[size_t(t) * k + j]) * H + n];
     out[size_t(t) * H + n] = acc;
   }
@@ -157,14 +171,15 @@ __global__ __launch_bounds__(256) void combine_f32(const float* __restrict__ yp,
 
 // sh: nsh fp32 slabs of shared-expert rows [T][H] (bf16-output recipes only; nsh = 0: none).
 hipError_t launch_combine_rows(const moe_config_t& c, const void* y_perm, const int32_t* pair_pos,
-                               const float* topk_w, const float* sh, int nsh, void* out, hipStream_t st) {
+                               const float* topk_w, const float* sh, int nsh, const void* resid, void* out,
+                               hipStream_t st) {
   if (c.recipe == MOE_RECIPE_F32)
     combine_f32<<<c.num_tokens, 256, 0, st>>>(static_cast<const float*>(y_perm), pair_pos, topk_w, c.top_k,
-                                              c.hidden, static_cast<float*>(out));
+                                              c.hidden, static_cast<const float*>(resid), static_cast<float*>(out));
   else
     combine_bf16<<<c.num_tokens, 256, 0, st>>>(static_cast<const uint16_t*>(y_perm), pair_pos, topk_w, sh, nsh,
                                                size_t(c.num_tokens) * c.hidden, c.top_k, c.hidden,
-                                               static_cast<uint16_t*>(out));
+                                               static_cast<const uint16_t*>(resid), static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 

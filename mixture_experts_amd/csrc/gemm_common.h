@@ -38,6 +38,7 @@ struct GemmArgs {
   // out + z * split_stride.
   size_t split_stride;
   // combine epilogue
+  const void* resid;        // residual rows added to the output (nullable)
   const void* y_perm;
   const int32_t* pair_pos;
   const float* topk_w;

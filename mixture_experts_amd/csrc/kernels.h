@@ -54,8 +54,11 @@ hipError_t launch_grouped_ffn(const moe_config_t& c, const int32_t* offsets, con
                               const void* x_perm_scale, const int32_t* a_map, const moe_weights_t& w, void* y_perm,
                               const FfnScratch& s, hipStream_t st);
 
+// resid (nullable): residual rows [T][H] added to the output.
 hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32_t* pair_pos, const float* topk_w,
-                          const void* x, const moe_weights_t* shared, void* out, void* h_shared, float* sh_out,
-                          float* sh_part, hipStream_t st);
+                          const void* x, const moe_weights_t* shared, const void* resid, void* out, void* h_shared,
+                          float* sh_out, float* sh_part, hipStream_t st);
+
+hipError_t launch_rmsnorm(const moe_config_t& c, const void* h, const float* w, float eps, void* x, hipStream_t st);
 
 }  // namespace moe

@@ -13,7 +13,8 @@ hipError_t launch_rs_swiglu(int recipe, int ms, int m_tiles, const GemmArgs& g, 
 hipError_t launch_rs_down(int recipe, int ms, int m_tiles, const GemmArgs& g, hipStream_t st, int ksplit);
 hipError_t launch_f32(int mode, int m_tiles, const GemmArgs& g, hipStream_t st);
 hipError_t launch_combine_rows(const moe_config_t& c, const void* y_perm, const int32_t* pair_pos,
-                               const float* topk_w, const float* sh, int nsh, void* out, hipStream_t st);
+                               const float* topk_w, const float* sh, int nsh, const void* resid, void* out,
+                               hipStream_t st);
 hipError_t launch_swiglu_slabs(const float* part, int nz, int T, int nes, int Is, float limit, uint16_t* h,
                                hipStream_t st);
 hipError_t launch_build_tiles2(const int32_t* offsets, int E, int thresh, int bm_large, int bm_small,
@@ -90,7 +91,7 @@ SharedSplit shared_split(const moe_config_t& c) {
 // Scratch layout; the same for every entry point so one size serves all of them.
 struct Layout {
   size_t logits, gate_partial, hist, tiles_l, tiles_s, h, h_scale, h_shared, sh_out, sh_part, idx, w, offsets, sorted,
-      pos, x_perm, x_perm_scale, y_perm, total;
+      pos, x_perm, x_perm_scale, y_perm, xn, total;
 };
 
 Layout layout(const moe_config_t& c) {
@@ -120,12 +121,15 @@ Layout layout(const moe_config_t& c) {
   L.x_perm = take(size_t(P * H) * routed_act_bytes(c));
   L.x_perm_scale = take(act_scale_bytes(c, P, H));
   L.y_perm = take(size_t(P * H) * act_bytes(c));
+  L.xn = take(size_t(T * H) * act_bytes(c));          // normalised rows (moe_forward_residual)
   L.total = o;
   return L;
 }
 
 template <typename T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 moe_status_t check_common(const moe_config_t* c, void* ws, size_t ws_bytes) {
   if (!valid_config(c)) return MOE_ERR_INVALID_ARGUMENT;
@@ -252,11 +256,11 @@ hipError_t launch_grouped_ffn(const moe_config_t& c, const int32_t* offsets, con
 }
 
 hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32_t* pair_pos, const float* topk_w,
-                          const void* x, const moe_weights_t* shared, void* out, void* h_shared, float* sh_out,
-                          float* sh_part, hipStream_t st) {
+                          const void* x, const moe_weights_t* shared, const void* resid, void* out, void* h_shared,
+                          float* sh_out, float* sh_part, hipStream_t st) {
   if (c.num_shared == 0) {
     ProfScope p(MOE_K_COMBINE, st);
-    return launch_combine_rows(c, y_perm, pair_pos, topk_w, nullptr, 0, out, st);
+    return launch_combine_rows(c, y_perm, pair_pos, topk_w, nullptr, 0, resid, out, st);
   }
   const int T = c.num_tokens, SI = c.num_shared * c.shared_intermediate;
   hipError_t e;
@@ -303,7 +307,7 @@ hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32
     }
     if (e != hipSuccess) return e;
     ProfScope p(MOE_K_COMBINE, st);
-    return launch_combine_rows(c, y_perm, pair_pos, topk_w, sh_part, ss.ks2, out, st);
+    return launch_combine_rows(c, y_perm, pair_pos, topk_w, sh_part, ss.ks2, resid, out, st);
   }
   const bool f32 = c.recipe == MOE_RECIPE_F32;
   const bool lds = !f32 && T >= 128;                  // LDS-staged kernel for prefill-sized token counts
@@ -336,6 +340,7 @@ hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32
   d.ldo = c.hidden;
   if (f32) {                                           // fp32: put-back sum fused into the down projection
     d.out = out;
+    d.resid = resid;
     d.y_perm = y_perm;
     d.pair_pos = pair_pos;
     d.topk_w = topk_w;
@@ -351,7 +356,7 @@ hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32
   }
   if (e != hipSuccess) return e;
   ProfScope p(MOE_K_COMBINE, st);
-  return launch_combine_rows(c, y_perm, pair_pos, topk_w, sh_out, 1, out, st);
+  return launch_combine_rows(c, y_perm, pair_pos, topk_w, sh_out, 1, resid, out, st);
 }
 
 // ---------------------------------------------------------------- instrumentation
@@ -378,6 +383,35 @@ void prof_end(int tag, hipStream_t st) {
 }  // namespace moe
 
 using namespace moe;
+
+// DeepseekV3MoE.forward on activation rows x, plus (resid != nullptr) the
+// residual rows added in the combine.
+static hipError_t forward_impl(const moe_config_t& c, const void* x, const void* resid, const float* gate_w,
+                               const float* bias, const moe_weights_t* experts, const moe_weights_t* shared,
+                               void* out, int32_t* topk_idx_out, float* topk_w_out, void* ws, hipStream_t st) {
+  const Layout L = layout(c);
+  int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.idx);
+  float* w = topk_w_out ? topk_w_out : at<float>(ws, L.w);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* pos = at<int32_t>(ws, L.pos);
+  void* x_perm = at<void>(ws, L.x_perm);
+  void* x_perm_scale = quantised(c) ? at<void>(ws, L.x_perm_scale) : nullptr;
+  void* y_perm = at<void>(ws, L.y_perm);
+  int32_t* sorted = at<int32_t>(ws, L.sorted);
+  hipError_t e = launch_route(c, x, gate_w, bias, idx, w, at<float>(ws, L.logits), at<double>(ws, L.gate_partial), st);
+  // Fused gather: the routed GEMMs read the token rows of x (or of its quantised
+  // copy, made once per token) through the sorted pair order, with no gathered copy.
+  if (e == hipSuccess) e = launch_permute(c, idx, x, offsets, sorted, pos, nullptr, nullptr, at<int32_t>(ws, L.hist), st);
+  if (e == hipSuccess && quantised(c)) e = launch_quantize_tokens(c, x, x_perm, x_perm_scale, st);
+  if (e == hipSuccess) {
+    FfnScratch sc{at<int32_t>(ws, L.tiles_l), at<int32_t>(ws, L.tiles_s), at<void>(ws, L.h), at<void>(ws, L.h_scale)};
+    e = launch_grouped_ffn(c, offsets, quantised(c) ? x_perm : x, x_perm_scale, sorted, *experts, y_perm, sc, st);
+  }
+  if (e == hipSuccess)
+    e = launch_combine(c, y_perm, pos, w, x, shared, resid, out, at<void>(ws, L.h_shared), at<float>(ws, L.sh_out),
+                       at<float>(ws, L.sh_part), st);
+  return e;
+}
 
 extern "C" {
 
@@ -437,7 +471,7 @@ moe_status_t moe_profile_stop(double* ms_out, int64_t* count_out, int32_t n_tags
 const char* moe_kernel_tag_name(int32_t tag) {
   static const char* names[MOE_K_COUNT] = {"gate_logits", "router", "perm_hist", "perm_scan", "perm_scatter",
                                            "gather", "tile_list", "ffn_gate_up", "ffn_down", "shared_gate_up",
-                                           "shared_down_combine", "combine"};
+                                           "shared_down_combine", "combine", "rmsnorm"};
   return (tag >= 0 && tag < MOE_K_COUNT) ? names[tag] : "unknown";
 }
 
@@ -484,7 +518,7 @@ moe_status_t moe_combine(const moe_config_t* cfg, const void* y_perm, const int3
   if (!y_perm || !pair_pos || !topk_w || !out) return MOE_ERR_INVALID_ARGUMENT;
   if (cfg->num_shared > 0 && (!x || !shared || !shared->w13 || !shared->w2)) return MOE_ERR_INVALID_ARGUMENT;
   const Layout L = layout(*cfg);
-  return to_status(launch_combine(*cfg, y_perm, pair_pos, topk_w, x, shared, out, at<void>(ws, L.h_shared),
+  return to_status(launch_combine(*cfg, y_perm, pair_pos, topk_w, x, shared, nullptr, out, at<void>(ws, L.h_shared),
                                   at<float>(ws, L.sh_out), at<float>(ws, L.sh_part), static_cast<hipStream_t>(stream)));
 }
 
@@ -495,29 +529,37 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* ga
   if (s != MOE_OK || cfg->num_tokens == 0) return s;
   if (!x || !gate_w || !bias || !out || !weights_ok(*cfg, experts)) return MOE_ERR_INVALID_ARGUMENT;
   if (cfg->num_shared > 0 && (!shared || !shared->w13 || !shared->w2)) return MOE_ERR_INVALID_ARGUMENT;
-  const moe_config_t& c = *cfg;
-  const Layout L = layout(c);
+  return to_status(forward_impl(*cfg, x, nullptr, gate_w, bias, experts, shared, out, topk_idx_out, topk_w_out, ws,
+                                static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_rmsnorm(const moe_config_t* cfg, const void* resid, const float* norm_w, float eps, void* x,
+                         void* stream) {
+  if (!valid_config(cfg)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!supported_shape(cfg)) return MOE_ERR_UNSUPPORTED;
+  if (!(eps >= 0.0f && eps <= 3.0e38f)) return MOE_ERR_INVALID_ARGUMENT;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if (!resid || !norm_w || !x || resid == x) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(resid) || !aligned16(norm_w) || !aligned16(x)) return MOE_ERR_INVALID_ARGUMENT;
+  return to_status(launch_rmsnorm(*cfg, resid, norm_w, eps, x, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_forward_residual(const moe_config_t* cfg, const void* resid, const float* norm_w, float eps,
+                                  const float* gate_w, const float* bias, const moe_weights_t* experts,
+                                  const moe_weights_t* shared, void* out, int32_t* topk_idx_out, float* topk_w_out,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t s = check_common(cfg, ws, ws_bytes);
+  if (s != MOE_OK) return s;
+  if (!(eps >= 0.0f && eps <= 3.0e38f)) return MOE_ERR_INVALID_ARGUMENT;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if (!resid || !norm_w || !gate_w || !bias || !out || !weights_ok(*cfg, experts)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(resid) || !aligned16(norm_w) || !aligned16(out)) return MOE_ERR_INVALID_ARGUMENT;
+  if (cfg->num_shared > 0 && (!shared || !shared->w13 || !shared->w2)) return MOE_ERR_INVALID_ARGUMENT;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.idx);
-  float* w = topk_w_out ? topk_w_out : at<float>(ws, L.w);
-  int32_t* offsets = at<int32_t>(ws, L.offsets);
-  int32_t* pos = at<int32_t>(ws, L.pos);
-  void* x_perm = at<void>(ws, L.x_perm);
-  void* x_perm_scale = quantised(c) ? at<void>(ws, L.x_perm_scale) : nullptr;
-  void* y_perm = at<void>(ws, L.y_perm);
-  int32_t* sorted = at<int32_t>(ws, L.sorted);
-  hipError_t e = launch_route(c, x, gate_w, bias, idx, w, at<float>(ws, L.logits), at<double>(ws, L.gate_partial), st);
-  // Fused gather: the routed GEMMs read the token rows of x (or of its quantised
-  // copy, made once per token) through the sorted pair order, with no gathered copy.
-  if (e == hipSuccess) e = launch_permute(c, idx, x, offsets, sorted, pos, nullptr, nullptr, at<int32_t>(ws, L.hist), st);
-  if (e == hipSuccess && quantised(c)) e = launch_quantize_tokens(c, x, x_perm, x_perm_scale, st);
-  if (e == hipSuccess) {
-    FfnScratch sc{at<int32_t>(ws, L.tiles_l), at<int32_t>(ws, L.tiles_s), at<void>(ws, L.h), at<void>(ws, L.h_scale)};
-    e = launch_grouped_ffn(c, offsets, quantised(c) ? x_perm : x, x_perm_scale, sorted, *experts, y_perm, sc, st);
-  }
+  void* xn = at<void>(ws, layout(*cfg).xn);
+  hipError_t e = launch_rmsnorm(*cfg, resid, norm_w, eps, xn, st);
   if (e == hipSuccess)
-    e = launch_combine(c, y_perm, pos, w, x, shared, out, at<void>(ws, L.h_shared), at<float>(ws, L.sh_out),
-                       at<float>(ws, L.sh_part), st);
+    e = forward_impl(*cfg, xn, resid, gate_w, bias, experts, shared, out, topk_idx_out, topk_w_out, ws, st);
   return to_status(e);
 }
 

@@ -50,8 +50,14 @@ reason in the design notes):
      and keeps the input's sign bit (a negative value that rounds to zero
      gives the code 0x80).
      The shared experts and the gate see the unquantised x.
-  R8 FFN in fp64 on the dequantised weights; no bias, no clamp; shared
-     experts are summed; the output excludes the residual.
+  R8 FFN in fp64 on the dequantised weights; no bias; shared experts are
+     summed; the output excludes the residual (the residual form below adds it).
+  R11 swiglu_limit (V4-Pro overview, FFN entry, named only): when > 0, every
+     SwiGLU computes SiLU(min(g, L)) * clamp(u, -L, L).
+  R12 residual form (walk-through 3.5 decoder layer; V4-Pro overview: RMSNorm
+     kept in fp32): x = post_attention_layernorm(h) with each row
+     (h * r) * weight, r = 1/sqrt(mean(h^2) + eps), evaluated in fp64, rounded to
+     fp32 and then to the activation format; out = h + MoE(x).
 """
 from __future__ import annotations
 
@@ -72,6 +78,13 @@ RECIPE_F32, RECIPE_BF16, RECIPE_FP8_B128, RECIPE_MXFP4 = 0, 1, 2, 3
 def decode_bf16(u16: np.ndarray) -> np.ndarray:
     """bfloat16 bit patterns (uint16) -> float64: the upper half of an fp32."""
     return (u16.astype(np.uint32) << 16).view(np.float32).astype(F64)
+
+
+def encode_bf16(v32: np.ndarray) -> np.ndarray:
+    """Finite fp32 values -> bfloat16 bit patterns, rounding to nearest, ties to even."""
+    u = np.ascontiguousarray(v32, dtype=F32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    return ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
 
 
 def _e4m3fn_table() -> np.ndarray:
@@ -374,6 +387,30 @@ def moe_forward(cfg, x64: np.ndarray, gate_w64: np.ndarray, bias32: np.ndarray,
         shared += expert_mlp(xa, shared_w13[s], shared_w2[s], limit=limit)
     return dict(out=routed + shared, y=y, routed=routed, shared=shared, routing=routing,
                 perm=perm, tokens=tokens)
+
+
+def rms_norm(h: np.ndarray, weight: np.ndarray, eps: float, recipe: int) -> np.ndarray:
+    """post_attention_layernorm over the rows of the residual stream h (R12).
+    Returns the stored rows' values as float64 (fp32 values, or bf16 values for the
+    other recipes)."""
+    h64 = np.asarray(h, dtype=F64)
+    r = 1.0 / np.sqrt((h64 * h64).sum(axis=1) / h64.shape[1] + float(eps))
+    y32 = ((h64 * r[:, None]) * np.asarray(weight, dtype=F64)[None, :]).astype(F32)
+    if recipe == RECIPE_F32:
+        return y32.astype(F64)
+    return decode_bf16(encode_bf16(y32))
+
+
+def moe_forward_residual(cfg, h64: np.ndarray, norm_w: np.ndarray, eps: float, gate_w64: np.ndarray,
+                         bias32: np.ndarray, expert_raw, shared_w13: np.ndarray, shared_w2: np.ndarray,
+                         tokens: np.ndarray | None = None):
+    """The decoder layer's MoE half (walk-through 3.5): out = h + MoE(RMSNorm(h))."""
+    x = rms_norm(h64, norm_w, eps, cfg.recipe)
+    r = moe_forward(cfg, x, gate_w64, bias32, expert_raw, shared_w13, shared_w2, tokens=tokens)
+    r["x"] = x
+    r["moe_out"] = r["out"]
+    r["out"] = np.asarray(h64, dtype=F64)[r["tokens"]] + r["out"]
+    return r
 
 
 def gather_rows(recipe: int, x32: np.ndarray, sorted_pair: np.ndarray, k: int):

@@ -433,3 +433,43 @@ def test_page_constants_and_mxfp4_byte_accounting():
     with_scales = st["params"] * O.mxfp4_bytes_per_param() / 1e12
     assert st["lower_bound_TB"] < with_scales < st["stored_TB"]
     assert st["params"] * 2 / 1e12 >= st["unquantised_16bit_TB_at_least"]
+
+
+# ------------------------------------------------------------------ residual form (RMSNorm)
+def test_encode_bf16_matches_torch_round_to_nearest_even():
+    rng = np.random.default_rng(15)
+    v = np.concatenate([rng.standard_normal(5000).astype(F32) * 10.0 ** rng.integers(-6, 6, 5000),
+                        # exact ties between two bf16 neighbours: low 16 bits 0x8000
+                        (rng.integers(0x3F000000, 0x40800000, 200).astype(np.uint32) & 0xFFFF0000 | 0x8000)
+                        .view(F32)]).astype(F32)
+    want = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.encode_bf16(v), want)
+
+
+@pytest.mark.parametrize("recipe", [O.RECIPE_F32, O.RECIPE_BF16])
+def test_rms_norm_closed_forms(recipe):
+    H = 256
+    # a constant row c: mean square c^2, so with eps = 0 and unit weight every entry is sign(c)
+    h = np.array([[0.75] * H, [-3.0] * H, [2.0 ** -20] * H])
+    np.testing.assert_array_equal(O.rms_norm(h, np.ones(H), 0.0, recipe), np.sign(h))
+    # an all-zero row stays zero when eps > 0 (no NaN)
+    assert np.array_equal(O.rms_norm(np.zeros((2, H)), np.ones(H), 1e-6, recipe), np.zeros((2, H)))
+    # scale invariance: multiplying a row by a power of two changes nothing (eps = 0)
+    rng = np.random.default_rng(16)
+    r = rng.standard_normal((5, H)).astype(F32).astype(np.float64)
+    w = 1.0 + 0.1 * rng.standard_normal(H)
+    np.testing.assert_array_equal(O.rms_norm(r * 8.0, w, 0.0, recipe), O.rms_norm(r, w, 0.0, recipe))
+
+
+def test_rms_norm_has_unit_rms_and_applies_the_weight_per_channel():
+    rng = np.random.default_rng(17)
+    H = 384
+    h = rng.standard_normal((20, H)) * 3.0
+    x = O.rms_norm(h, np.ones(H), 0.0, O.RECIPE_F32)
+    np.testing.assert_allclose(np.sqrt((x * x).mean(axis=1)), 1.0, rtol=1e-6)
+    w = 1.0 + 0.1 * rng.standard_normal(H)
+    np.testing.assert_allclose(O.rms_norm(h, w, 0.0, O.RECIPE_F32), x * w[None, :], rtol=2e-7)
+    # eps enters under the root: a row with mean square m gets the factor 1/sqrt(m + eps)
+    xe = O.rms_norm(h, np.ones(H), 0.5, O.RECIPE_F32)
+    m = (h * h).mean(axis=1)
+    np.testing.assert_allclose(xe, h / np.sqrt(m + 0.5)[:, None], rtol=2e-7)

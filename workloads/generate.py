@@ -34,7 +34,11 @@ E4M3_MAX = 448.0
 E2M1_MAX = 6.0
 
 TENSOR_IDS = {"x": 1, "gate_w": 2, "bias": 3, "w13": 4, "w2": 5, "shared_w13": 6, "shared_w2": 7,
-              "zipf_perm": 8}
+              "zipf_perm": 8, "norm_w": 9}
+
+# post_attention_layernorm epsilon of the residual form (not stated by the pages;
+# the usual DeepSeek config value)
+RMS_EPS = 1e-6
 
 
 def tensor_seed(cfg: C.MoEConfig, tensor: str, expert: int = 0) -> int:
@@ -147,6 +151,7 @@ class MoEInputs:
     w2_scale: torch.Tensor | None    # fp8: [E, H/128, I/128] fp32; MX: [E, H, I/32] uint8
     shared_w13: torch.Tensor         # [S, 2Is, H] fp32 or bf16
     shared_w2: torch.Tensor          # [S, H, Is]
+    norm_w: torch.Tensor | None = None   # [H] fp32 post_attention_layernorm weight (residual form)
     meta: dict = field(default_factory=dict)
 
 
@@ -206,7 +211,9 @@ def generate(cfg: C.MoEConfig, device="cpu", experts: bool = True) -> MoEInputs:
     for s in range(S):
         sw13[s].copy_(normal(cfg, "shared_w13", s, (2 * Is, H), cfg.expert_std, device).to(sh_dtype))
         sw2[s].copy_(normal(cfg, "shared_w2", s, (H, Is), cfg.expert_std, device).to(sh_dtype))
-    return MoEInputs(cfg, x, gate_w, bias, w13, w2, w13s, w2s, sw13, sw2)
+    # RMSNorm weight of the residual form: near 1, like a trained norm
+    norm_w = (1.0 + normal(cfg, "norm_w", 0, (H,), 0.1)).to(device)
+    return MoEInputs(cfg, x, gate_w, bias, w13, w2, w13s, w2s, sw13, sw2, norm_w)
 
 
 def expert_weight_bytes(cfg: C.MoEConfig) -> int:
