@@ -23,7 +23,7 @@ sys.path.insert(0, ROOT)
 
 PEAK = {  # MI355X published peaks (dense)
     "hbm_GBps": 8000.0,
-    "bf16_TFLOPs": 2516.6, "fp8_TFLOPs": 5033.2, "mxfp4_TFLOPs": 10066.3, "fp32_TFLOPs": 157.3,
+    "bf16_TFLOPs": 2516.6, "fp16_TFLOPs": 2516.6, "fp8_TFLOPs": 5033.2, "mxfp4_TFLOPs": 10066.3, "fp32_TFLOPs": 157.3,
 }
 
 
@@ -67,6 +67,8 @@ def dominant_kernel_work(cfg, counts):
         wbytes, abytes = 4 * n, 4
     elif cfg.recipe == C.RECIPE_FP8_B128:
         wbytes, abytes = n + 4 * n // (128 * 128), 1
+    elif cfg.recipe == C.RECIPE_NVFP4:
+        wbytes, abytes = n // 2 + n // 16, 2
     else:
         wbytes, abytes = n // 2 + n // 32, 1
     bytes_ = touched * wbytes + P * H * abytes + P * I * abytes
@@ -175,7 +177,7 @@ def main():
     touched, kbytes, kflops, wbytes = dominant_kernel_work(cfg, counts)
     ms_k, n_k = prof["ffn_gate_up"]
     avg_k = ms_k / max(n_k, 1)
-    hbm_bound = cfg.name in ("decode_bf16", "finegrained_mxfp4", "tiny_fp32")
+    hbm_bound = cfg.name in ("decode_bf16", "finegrained_mxfp4", "tiny_fp32", "decode_nvfp4")
     src_hash = kernel_source_hash()
     traffic = traffic_from_profiles(cfg.name, src_hash)
     if hbm_bound:
@@ -183,7 +185,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_GBps"], "unit": "GB/s"}
     else:
         pk = {C.RECIPE_BF16: "bf16_TFLOPs", C.RECIPE_FP8_B128: "fp8_TFLOPs", C.RECIPE_MXFP4: "mxfp4_TFLOPs",
-              C.RECIPE_F32: "fp32_TFLOPs"}[cfg.recipe]
+              C.RECIPE_F32: "fp32_TFLOPs", C.RECIPE_NVFP4: "fp16_TFLOPs"}[cfg.recipe]
         achieved = kflops / (avg_k * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK[pk], "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
@@ -193,7 +195,7 @@ def main():
     roof["algorithmic_per_launch"] = kbytes if hbm_bound else kflops
 
     dtype = {C.RECIPE_F32: "f32", C.RECIPE_BF16: "bf16", C.RECIPE_FP8_B128: "fp8_e4m3",
-             C.RECIPE_MXFP4: "mxfp4xmxfp8"}[cfg.recipe]
+             C.RECIPE_MXFP4: "mxfp4xmxfp8", C.RECIPE_NVFP4: "nvfp4 (fp16 MFMA)"}[cfg.recipe]
     line = {
         "metric": "MoE-layer tokens/s (one layer forward, 1 GPU)",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -58,6 +58,16 @@
  *                        amax <= 448 * 2^e (MXFP4 weights with MXFP8
  *                        activations: ruibaoantu.com 2.8T articles,
  *                        quantisation section); shared weights, y_perm, out bf16.
+ *   MOE_RECIPE_NVFP4     x bf16; routed weights NVFP4 = e2m1 packed two per byte
+ *                        (low nibble = even column) with one e4m3fn scale code
+ *                        per 16 along the input dimension; routed-expert
+ *                        activations NVFP4 per (row, 16 channels) with scale
+ *                        e4m3(amax/6) (1 when that rounds to 0) and elements
+ *                        e2m1(v/scale), stored as their fp16 values (exact):
+ *                        x_perm is fp16 [T*k][H] and x_perm_scale unused (weights
+ *                        and input activations in 4 bits with an FP8 scale per
+ *                        16: walk-through section 4; shared experts excluded);
+ *                        shared weights, y_perm, out bf16.
  *   The gate weight and the correction bias are fp32 in every recipe.
  */
 #ifndef MOE_MI355X_H
@@ -84,7 +94,8 @@ typedef enum {
   MOE_RECIPE_F32 = 0,
   MOE_RECIPE_BF16 = 1,
   MOE_RECIPE_FP8_B128 = 2,
-  MOE_RECIPE_MXFP4 = 3
+  MOE_RECIPE_MXFP4 = 3,
+  MOE_RECIPE_NVFP4 = 4
 } moe_recipe_t;
 
 /* Layer shape and routing hyper-parameters (names follow the config.json keys
@@ -121,10 +132,11 @@ typedef struct {
 
 /* One set of experts, expert-major and contiguous.
  *   w13: [n][2*I][H]  rows 0..I-1 are gate_proj, rows I..2I-1 are up_proj
- *        (MXFP4: [n][2*I][H/2] bytes);
- *   w2:  [n][H][I]    down_proj (MXFP4: [n][H][I/2] bytes);
+ *        (MXFP4, NVFP4: [n][2*I][H/2] bytes);
+ *   w2:  [n][H][I]    down_proj (MXFP4, NVFP4: [n][H][I/2] bytes);
  *   w13_scale, w2_scale: FP8_B128: fp32 [n][2I/128][H/128] and [n][H/128][I/128];
  *                        MXFP4: E8M0 bytes [n][2I][H/32] and [n][H][I/32];
+ *                        NVFP4: e4m3fn codes [n][2I][H/16] and [n][H][I/16];
  *                        other recipes: unused (may be NULL).
  * n = num_experts for routed experts; n = num_shared for the shared experts,
  * whose I is shared_intermediate and which always use the plain (F32 or BF16)

@@ -14,6 +14,8 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) double f64x4;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 
 constexpr int kWave = 64;
 
@@ -58,6 +60,38 @@ __device__ __forceinline__ float exp2i(int e) {      // 2^e for e in [-149, 127]
   if (e >= -126) return __uint_as_float(uint32_t(e + 127) << 23);
   return __uint_as_float(1u << (e + 149));
 }
+
+// ------------------------------------------------------------------ NVFP4 (e2m1 + e4m3 per 16)
+// e4m3fn code -> value (finite codes; exact in fp32).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : float(m) * 0.001953125f;   // m * 2^-9
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// e2m1 code of v: nearest grid value (0, 0.5, 1, 1.5, 2, 3, 4, 6), ties to the even
+// code, saturating at 6; the sign bit is kept.
+__device__ __forceinline__ uint32_t f32_to_e2m1(float v) {
+  const float a = fabsf(v);
+  const uint32_t c = uint32_t(a > 0.25f) + uint32_t(a >= 0.75f) + uint32_t(a > 1.25f) + uint32_t(a >= 1.75f) +
+                     uint32_t(a > 2.5f) + uint32_t(a >= 3.5f) + uint32_t(a > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+  const uint32_t m = c & 7u;
+  const float mag = m < 2u ? 0.5f * float(m) : __uint_as_float(((m >> 1) + 126u) << 23) * ((m & 1u) ? 1.5f : 1.0f);
+  return (c & 8u) ? -mag : mag;
+}
+
+// Scale of an NVFP4 group from its amax: e4m3(amax / 6), or 1 when that rounds to 0.
+__device__ __forceinline__ float nvfp4_scale(float amax) {
+  const float s = e4m3_to_f32(f32_to_e4m3(amax / 6.0f));
+  return s > 0.0f ? s : 1.0f;
+}
+
+// NVFP4 value of v in a group of scale s: e2m1(v / s) * s, exact in fp32 and fp16.
+__device__ __forceinline__ float nvfp4_value(float v, float s) { return e2m1_to_f32(f32_to_e2m1(v / s)) * s; }
 
 // Least integer e with amax <= 448 * 2^e (amax >= 0 finite); 0 for amax == 0; clamped to [-127, 127].
 __device__ __forceinline__ int mx_exponent_e4m3(float amax) {

@@ -23,7 +23,12 @@
 //             on gfx950: an fp8 operand lane (half h) holds K = 16h + 0..15 and
 //             32 + 16h + 0..15, an fp4 operand lane holds K = 32h + 0..31 (even K in
 //             the low nibble), and the scale of lane (row, h) applies to K block h.
-// The SwiGLU output h is written as bf16, or re-quantised to the activation format.
+//   nvfp4     v_mfma_f32_32x32x16_f16 on exactly dequantised operands: activations
+//             arrive as the fp16 values of their NVFP4 quantisation; e2m1 weights
+//             are turned into fp16 in registers (byte lookup of the fp16 high byte,
+//             times the group's e4m3 scale: every such product is exact in fp16).
+// The SwiGLU output h is written as bf16, or re-quantised to the activation format
+// (NVFP4: stored as fp16 values).
 #include "gemm_common.h"
 #include "kernels.h"
 
@@ -49,6 +54,26 @@ __device__ __forceinline__ void rs_copy16(const void* g, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_wave_base, 16, 0, 0);
 }
 
+// Eight e2m1 codes (one dword, low nibble = lower k) times an fp16 scale pair ->
+// eight fp16 values in k order.  The magnitudes index a byte table of the fp16
+// high bytes (the low byte of every e2m1 value in fp16 is zero); the sign bit of
+// each nibble becomes the fp16 sign.
+__device__ __forceinline__ f16x8 e2m1x8_to_f16(uint32_t w, f16x2 scale) {
+  constexpr uint32_t T_LO = 0x3E3C3800u, T_HI = 0x46444240u;   // 0, .5, 1, 1.5 | 2, 3, 4, 6
+  const uint32_t he = __builtin_amdgcn_perm(T_HI, T_LO, w & 0x07070707u) | ((w << 4) & 0x80808080u);   // even k
+  const uint32_t ho = __builtin_amdgcn_perm(T_HI, T_LO, (w >> 4) & 0x07070707u) | (w & 0x80808080u);   // odd k
+  f16x8 out;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    // bytes: 0, even k = 2q high byte, 0, odd k = 2q+1 high byte
+    const uint32_t d = __builtin_amdgcn_perm(ho, he, 0x040C000Cu + 0x01000100u * q);
+    const f16x2 v = __builtin_bit_cast(f16x2, d) * scale;
+    out[2 * q] = v[0];
+    out[2 * q + 1] = v[1];
+  }
+  return out;
+}
+
 __device__ __forceinline__ i32x8 rs_cat(uint4 lo, uint4 hi) {
   return i32x8{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
 }
@@ -62,11 +87,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   constexpr bool BF16 = RECIPE == MOE_RECIPE_BF16;
   constexpr bool MX = RECIPE == MOE_RECIPE_MXFP4;
   constexpr bool FP8 = RECIPE == MOE_RECIPE_FP8_B128;
-  constexpr int EA = BF16 ? 2 : 1;                 // activation bytes per element
+  constexpr bool NV = RECIPE == MOE_RECIPE_NVFP4;
+  constexpr bool FP4 = MX || NV;                   // packed e2m1 weights with per-row scale bytes
+  constexpr bool ASC = FP8 || MX;                  // activations as codes plus row scales
+  constexpr int EA = (BF16 || NV) ? 2 : 1;         // activation bytes per element (NVFP4: fp16 values)
   constexpr int KS = RS_ROWB / EA;                 // K per stage
-  constexpr int WB = MX ? 2 : 1;                   // weight elements per byte (fp4: 2)
+  constexpr int WB = FP4 ? 2 : 1;                  // weight elements per byte (fp4: 2)
   constexpr int EBW = BF16 ? 2 : 1;                // weight bytes per element (bf16 2, fp8 1; fp4 via WB)
-  constexpr int BCH = MX ? 2 : 4;                  // 16-byte weight chunks per fragment and stage
+  constexpr int BCH = MX ? 2 : (NV ? 1 : 4);       // 16-byte weight chunks per fragment and stage
+  constexpr int SG = MX ? 32 : 16;                 // fp4 scale group along K
   constexpr int A_INSTR = MS;                      // async copies per wave per stage: BM*8 chunks / 256 lanes
   __shared__ __attribute__((aligned(1024))) uint8_t As[NST][BM * RS_ROWB];
   __shared__ uint32_t Sa[NST][BM];                 // fp8: fp32 row scale bits; MX: 4 E8M0 bytes
@@ -97,7 +126,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     n0 = nt * 128;
     sub0 = ti.e * g.n_experts_split + n0 / ns;
     const int nl = n0 % ns + wave * 32 + l32;
-    const size_t rowbytes = MX ? size_t(K) / 2 : size_t(K) * EBW;
+    const size_t rowbytes = FP4 ? size_t(K) / 2 : size_t(K) * EBW;
     const uint8_t* base = B + size_t(sub0) * 2 * ns * rowbytes;
     brow[0] = base + size_t(nl) * rowbytes;
     brow[1] = base + size_t(ns + nl) * rowbytes;
@@ -108,7 +137,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     wave_on = n0 + wave * 64 < g.N;
     const int n = min(n0 + wave * 64 + l32, g.N - 1);
     const int n1 = min(n + 32, g.N - 1);
-    const size_t rowbytes = MX ? size_t(ns) / 2 : size_t(ns) * EBW;
+    const size_t rowbytes = FP4 ? size_t(ns) / 2 : size_t(ns) * EBW;
     const uint8_t* base = B + size_t(ti.e) * g.n_experts_split * g.N * rowbytes;
     brow[0] = base + size_t(n) * rowbytes;
     brow[1] = base + size_t(n1) * rowbytes;
@@ -117,14 +146,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   }
   // byte offset of K position k0 inside a weight row (down: plus the sub-expert stride)
   auto koff = [&](int k0) -> size_t {
-    if (MODE == EPI_SWIGLU) return MX ? size_t(k0) / 2 : size_t(k0) * EBW;
-    const size_t sub_stride = MX ? size_t(g.N) * ns / 2 : size_t(g.N) * ns * EBW;
-    return size_t(k0 / ns) * sub_stride + (MX ? size_t(k0 % ns) / 2 : size_t(k0 % ns) * EBW);
+    if (MODE == EPI_SWIGLU) return FP4 ? size_t(k0) / 2 : size_t(k0) * EBW;
+    const size_t sub_stride = FP4 ? size_t(g.N) * ns / 2 : size_t(g.N) * ns * EBW;
+    return size_t(k0 / ns) * sub_stride + (FP4 ? size_t(k0 % ns) / 2 : size_t(k0 % ns) * EBW);
   };
   // this lane's weight bytes for the stage at k0, per fragment: bf16 and fp8 64
   // contiguous bytes at 64h; MX two 16-byte pieces at 32s + 16h
   auto bsrc = [&](int f, int k0) -> const uint8_t* {
-    return brow[f] + koff(k0) + (MX ? half * 16 : half * 64);
+    return brow[f] + koff(k0) + (FP4 ? half * 16 : half * 64);
   };
   auto bscale_fp8 = [&](int f, int k0) -> float {
     const float* S = static_cast<const float*>(g.B_scale);
@@ -136,13 +165,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     const int cb = min(n0 + wave * 64 + f * 32, g.N - 1) / 128;
     return S[(size_t(sub) * (g.N / 128) + cb) * (ns / 128) + (k0 % ns) / 128];
   };
-  // MX weight scales of fragment f at k0: 4 E8M0 bytes (blocks k0/32 .. +3) of this lane's row
-  auto bscale_mx = [&](int f, int k0) -> uint32_t {
+  // fp4 weight scales of fragment f at k0: 4 scale bytes (groups k0/SG .. +3) of this
+  // lane's row: MX E8M0 per 32, NVFP4 e4m3 codes per 16
+  auto bscale_fp4 = [&](int f, int k0) -> uint32_t {
     const uint8_t* S = static_cast<const uint8_t*>(g.B_scale);
     if (MODE == EPI_SWIGLU)
-      return *reinterpret_cast<const uint32_t*>(S + (size_t(sub0) * 2 * ns + ncol[f]) * (K / 32) + k0 / 32);
+      return *reinterpret_cast<const uint32_t*>(S + (size_t(sub0) * 2 * ns + ncol[f]) * (K / SG) + k0 / SG);
     const int sub = ti.e * g.n_experts_split + k0 / ns;
-    return *reinterpret_cast<const uint32_t*>(S + (size_t(sub) * g.N + ncol[f]) * (ns / 32) + (k0 % ns) / 32);
+    return *reinterpret_cast<const uint32_t*>(S + (size_t(sub) * g.N + ncol[f]) * (ns / SG) + (k0 % ns) / SG);
   };
 
   // ---- activation copies: copy j of wave w fills LDS chunk positions (w*MS + j)*64 + lane
@@ -152,7 +182,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     const int p = (wave * A_INSTR + j) * 64 + lane, r = p >> 3, c = rs_slot(r, p & 7);
     a_src[j] = A + size_t(a_row(g, ti.row0 + min(r, ti.rows - 1))) * g.lda * EA + c * 16;
   }
-  const int sa_row = BF16 ? 0 : a_row(g, ti.row0 + min(tid % BM, ti.rows - 1));
+  const int sa_row = ASC ? a_row(g, ti.row0 + min(tid % BM, ti.rows - 1)) : 0;
   auto load_sa = [&](int k0) -> uint32_t {        // every thread loads (rows clamped): equal vmcnt per wave
     if (MX) return *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(g.A_scale) +
                                                       size_t(sa_row) * (K / 32) + k0 / 32);
@@ -166,7 +196,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
 #pragma unroll
     for (int j = 0; j < A_INSTR; ++j)
       rs_copy16(a_src[j] + size_t(k0) * EA, &As[buf][(wave * A_INSTR + j) * 1024]);
-    if (!BF16) sreg[buf] = load_sa(k0);
+    if (ASC) sreg[buf] = load_sa(k0);
     // every wave loads (inactive column waves read a clamped, valid row) so that all
     // waves count the same loads per stage
 #pragma unroll
@@ -174,10 +204,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
       const uint8_t* p = bsrc(f, k0);
 #pragma unroll
       for (int c = 0; c < BCH; ++c) breg[buf][f][c] = *reinterpret_cast<const uint4*>(p + c * (MX ? 32 : 16));
-      if (MX) sbm[buf][f] = bscale_mx(f, k0);
+      if (FP4) sbm[buf][f] = bscale_fp4(f, k0);
     }
   };
-  constexpr int PER_STAGE = A_INSTR + (BF16 ? 0 : 1) + 2 * BCH + (MX ? 2 : 0);   // loads per stage per thread
+  constexpr int PER_STAGE = A_INSTR + (ASC ? 1 : 0) + 2 * BCH + (FP4 ? 2 : 0);   // loads per stage per thread
 
   f32x16 acc[MS][2];
 #pragma unroll
@@ -221,6 +251,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
                   __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Ab + rs_swz(i * 32 + l32, half * 4 + s)));
               acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[i][0], 0, 0, 0);
               acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[i][1], 0, 0, 0);
+            }
+          }
+        }
+      } else if (NV) {
+        // fp16 MFMA on exactly dequantised operands: the activations are fp16 values
+        // already; the weights' e2m1 codes become fp16 by a byte lookup, times the
+        // group's e4m3 scale (every product is exact in fp16).  Lane half h, step s
+        // takes k = 32h + 8s .. +8 on both sides: step s uses dword s of the lane's
+        // 16 weight bytes and scale byte 2h + s/2 of the stage's four.
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          f16x8 bw[2];
+#pragma unroll
+          for (int f = 0; f < 2; ++f) {
+            const uint32_t w = (s == 0) ? breg[buf][f][0].x : (s == 1) ? breg[buf][f][0].y
+                             : (s == 2) ? breg[buf][f][0].z : breg[buf][f][0].w;
+            const _Float16 sc = _Float16(e4m3_to_f32((sbm[buf][f] >> (8 * (2 * half + (s >> 1)))) & 0xffu));
+            bw[f] = e2m1x8_to_f16(w, f16x2{sc, sc});
+          }
+#pragma unroll
+          for (int i = 0; i < MS; ++i) {
+            if (i < act_ms) {
+              const f16x8 a =
+                  __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(Ab + rs_swz(i * 32 + l32, half * 4 + s)));
+              acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bw[0], a, acc[i][0], 0, 0, 0);
+              acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bw[1], a, acc[i][1], 0, 0, 0);
             }
           }
         }
@@ -328,6 +384,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
                 uint8_t(e + 127);
         }
       }
+    } else if (NV) {                               // NVFP4 per (row, 16 columns), stored as fp16 values
+      uint16_t* Hf = static_cast<uint16_t*>(g.out);
+#pragma unroll
+      for (int i = 0; i < MS; ++i) {
+        if (i >= act_ms) continue;
+        float hv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) hv[r] = swiglu_f32(acc[i][0][r], acc[i][1][r], g.swiglu_limit);
+        // group j (columns 16j .. 16j+15) = registers 8j .. 8j+7 of both lane halves
+        float sc[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float m = 0.0f;
+#pragma unroll
+          for (int r = 8 * j; r < 8 * j + 8; ++r) m = fmaxf(m, fabsf(hv[r]));
+          sc[j] = nvfp4_scale(fmaxf(m, __shfl_xor(m, 32, 64)));
+        }
+        const int row = i * 32 + l32;
+        if (row < ti.rows) {
+          uint16_t* hrow = Hf + size_t(ti.row0 + row) * g.ldo + c0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float s = sc[q >> 1];
+            const f16x2 lo = {_Float16(nvfp4_value(hv[4 * q], s)), _Float16(nvfp4_value(hv[4 * q + 1], s))};
+            const f16x2 hi = {_Float16(nvfp4_value(hv[4 * q + 2], s)), _Float16(nvfp4_value(hv[4 * q + 3], s))};
+            *reinterpret_cast<uint2*>(hrow + 8 * q) = uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+          }
+        }
+      }
     } else {                                       // fp8 per (row, 128 columns): across the four waves
       uint8_t* Hq = static_cast<uint8_t*>(g.out);
 #pragma unroll
@@ -414,7 +499,8 @@ static void rs_launch(int ms, dim3 grid, const GemmArgs& g, hipStream_t st) {
       return;
     }
   }
-  if (ms <= 1) ffn_rs_kernel<1, MODE, RECIPE, RS_NST1><<<grid, 256, 0, st>>>(g);
+  // NVFP4 moves 0.56 weight bytes per element: a deeper ring keeps enough of them in flight
+  if (ms <= 1) ffn_rs_kernel<1, MODE, RECIPE, (RECIPE == MOE_RECIPE_NVFP4 ? 6 : RS_NST1)><<<grid, 256, 0, st>>>(g);
   else ffn_rs_kernel<2, MODE, RECIPE, RS_NST2, (RECIPE == MOE_RECIPE_FP8_B128 ? 2 : 1)><<<grid, 256, 0, st>>>(g);
 }
 
@@ -422,11 +508,12 @@ template <int MODE>
 static hipError_t rs_launch_recipe(int recipe, int ms, dim3 grid, const GemmArgs& g, hipStream_t st) {
   if (recipe == MOE_RECIPE_BF16) rs_launch<MODE, MOE_RECIPE_BF16>(ms, grid, g, st);
   else if (recipe == MOE_RECIPE_FP8_B128) rs_launch<MODE, MOE_RECIPE_FP8_B128>(ms, grid, g, st);
+  else if (recipe == MOE_RECIPE_NVFP4) rs_launch<MODE, MOE_RECIPE_NVFP4>(ms, grid, g, st);
   else rs_launch<MODE, MOE_RECIPE_MXFP4>(ms, grid, g, st);
   return hipGetLastError();
 }
 
-// Tiles of ms*32 rows (ms = 1 or 2; bf16 and MXFP4 also 4).  bf16 is used for the shared experts of every
+// Tiles of ms*32 rows (ms = 1 or 2; bf16, MXFP4 and NVFP4 also 4).  bf16 is used for the shared experts of every
 // bf16-activation recipe as well.
 hipError_t launch_rs_swiglu(int recipe, int ms, int m_tiles, const GemmArgs& g, hipStream_t st) {
   return rs_launch_recipe<EPI_SWIGLU>(recipe, ms, dim3(g.N / 128, m_tiles), g, st);

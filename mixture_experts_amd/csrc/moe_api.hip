@@ -34,7 +34,7 @@ bool valid_config(const moe_config_t* c) {
   if (c->n_group > 1 && c->num_experts / c->n_group < 2) return false;
   if (int64_t(c->topk_group) * (c->num_experts / c->n_group) < c->top_k) return false;
   if (c->score_func != MOE_SCORE_SIGMOID && c->score_func != MOE_SCORE_SQRTSOFTPLUS) return false;
-  if (c->recipe < MOE_RECIPE_F32 || c->recipe > MOE_RECIPE_MXFP4) return false;
+  if (c->recipe < MOE_RECIPE_F32 || c->recipe > MOE_RECIPE_NVFP4) return false;
   if (!(c->routed_scaling_factor == c->routed_scaling_factor)) return false;
   if (int64_t(c->num_tokens) * c->top_k > (int64_t(1) << 30)) return false;
   if (!(c->swiglu_limit >= 0.0f && c->swiglu_limit <= 3.0e38f)) return false;   // finite, >= 0
@@ -50,7 +50,8 @@ bool supported_shape(const moe_config_t* c) {
 
 size_t act_bytes(const moe_config_t& c) { return c.recipe == MOE_RECIPE_F32 ? 4 : 2; }     // x, y, out
 size_t routed_act_bytes(const moe_config_t& c) {                                             // x_perm, h
-  return c.recipe == MOE_RECIPE_F32 ? 4 : (c.recipe == MOE_RECIPE_BF16 ? 2 : 1);
+  // NVFP4 rows are kept as their fp16 values
+  return c.recipe == MOE_RECIPE_F32 ? 4 : ((c.recipe == MOE_RECIPE_BF16 || c.recipe == MOE_RECIPE_NVFP4) ? 2 : 1);
 }
 size_t act_scale_bytes(const moe_config_t& c, int64_t rows, int64_t cols) {
   if (c.recipe == MOE_RECIPE_FP8_B128) return size_t(rows * (cols / 128) * 4);
@@ -140,7 +141,12 @@ moe_status_t check_common(const moe_config_t* c, void* ws, size_t ws_bytes) {
   return MOE_OK;
 }
 
-bool quantised(const moe_config_t& c) { return c.recipe == MOE_RECIPE_FP8_B128 || c.recipe == MOE_RECIPE_MXFP4; }
+// Routed experts with quantised weights and activations.
+bool quantised(const moe_config_t& c) {
+  return c.recipe == MOE_RECIPE_FP8_B128 || c.recipe == MOE_RECIPE_MXFP4 || c.recipe == MOE_RECIPE_NVFP4;
+}
+// Quantised activations stored as codes plus a separate scale array (x_perm_scale).
+bool act_scaled(const moe_config_t& c) { return c.recipe == MOE_RECIPE_FP8_B128 || c.recipe == MOE_RECIPE_MXFP4; }
 
 bool weights_ok(const moe_config_t& c, const moe_weights_t* w) {
   if (!w || !w->w13 || !w->w2) return false;
@@ -170,11 +176,12 @@ FfnPlan ffn_plan(const moe_config_t& c) {
   const int64_t avg = P / std::max<int64_t>(1, E);
   p.bm_s = avg <= 40 ? 32 : 64;
   // Size the register-streaming tiles so that a typical expert takes one tile and
-  // its weights stream from HBM once: MXFP4 has no large-tile list; bf16 sends only
+  // its weights stream from HBM once: MXFP4 and NVFP4 have no large-tile list; bf16 sends only
   // experts under 128 rows there.  (fp8's 128-row variant spills registers.)
-  if (c.recipe == MOE_RECIPE_MXFP4) p.bm_s = avg <= 24 ? 32 : avg <= 48 ? 64 : 128;
+  const bool fp4w = c.recipe == MOE_RECIPE_MXFP4 || c.recipe == MOE_RECIPE_NVFP4;
+  if (fp4w) p.bm_s = avg <= 24 ? 32 : avg <= 48 ? 64 : 128;
   else if (c.recipe == MOE_RECIPE_BF16 && avg > 48) p.bm_s = 128;
-  p.thresh = (c.recipe == MOE_RECIPE_MXFP4) ? INT32_MAX : 128;
+  p.thresh = fp4w ? INT32_MAX : 128;
   p.bm_l = 256;
   p.max_l = (p.thresh == INT32_MAX || P < p.thresh) ? 0 : int((P + p.bm_l - 1) / p.bm_l + std::min<int64_t>(E, P / p.thresh));
   const int64_t small_bound = (p.thresh == INT32_MAX) ? (P + p.bm_s - 1) / p.bm_s + E
@@ -395,7 +402,7 @@ static hipError_t forward_impl(const moe_config_t& c, const void* x, const void*
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* pos = at<int32_t>(ws, L.pos);
   void* x_perm = at<void>(ws, L.x_perm);
-  void* x_perm_scale = quantised(c) ? at<void>(ws, L.x_perm_scale) : nullptr;
+  void* x_perm_scale = act_scaled(c) ? at<void>(ws, L.x_perm_scale) : nullptr;
   void* y_perm = at<void>(ws, L.y_perm);
   int32_t* sorted = at<int32_t>(ws, L.sorted);
   hipError_t e = launch_route(c, x, gate_w, bias, idx, w, at<float>(ws, L.logits), at<double>(ws, L.gate_partial), st);
@@ -491,7 +498,7 @@ moe_status_t moe_permute(const moe_config_t* cfg, const int32_t* topk_idx, const
   moe_status_t s = check_common(cfg, ws, ws_bytes);
   if (s != MOE_OK || cfg->num_tokens == 0) return s;
   if (!topk_idx || !x || !expert_offsets || !sorted_pair || !pair_pos || !x_perm) return MOE_ERR_INVALID_ARGUMENT;
-  if (quantised(*cfg) && !x_perm_scale) return MOE_ERR_INVALID_ARGUMENT;
+  if (act_scaled(*cfg) && !x_perm_scale) return MOE_ERR_INVALID_ARGUMENT;
   const Layout L = layout(*cfg);
   return to_status(launch_permute(*cfg, topk_idx, x, expert_offsets, sorted_pair, pair_pos, x_perm, x_perm_scale,
                                   at<int32_t>(ws, L.hist), static_cast<hipStream_t>(stream)));
@@ -503,7 +510,7 @@ moe_status_t moe_grouped_ffn(const moe_config_t* cfg, const int32_t* expert_offs
   moe_status_t s = check_common(cfg, ws, ws_bytes);
   if (s != MOE_OK || cfg->num_tokens == 0) return s;
   if (!expert_offsets || !x_perm || !y_perm || !weights_ok(*cfg, experts)) return MOE_ERR_INVALID_ARGUMENT;
-  if (quantised(*cfg) && !x_perm_scale) return MOE_ERR_INVALID_ARGUMENT;
+  if (act_scaled(*cfg) && !x_perm_scale) return MOE_ERR_INVALID_ARGUMENT;
   const Layout L = layout(*cfg);
   FfnScratch sc{at<int32_t>(ws, L.tiles_l), at<int32_t>(ws, L.tiles_s), at<void>(ws, L.h), at<void>(ws, L.h_scale)};
   return to_status(launch_grouped_ffn(*cfg, expert_offsets, x_perm, x_perm_scale, nullptr, *experts, y_perm, sc,

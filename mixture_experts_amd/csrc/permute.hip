@@ -113,6 +113,33 @@ __global__ __launch_bounds__(256) void perm_gather(const void* __restrict__ xv, 
     for (int c = lane; c < H / 8; c += 64) dst[c] = src[c];
     return;
   }
+  if (RECIPE == MOE_RECIPE_NVFP4) {                   // fp16 values of the NVFP4 rows: 16 channels = 2 lanes
+    uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(outv) + size_t(p) * H);
+    for (int c0 = 0; c0 < H / 8; c0 += 64) {
+      const int c = c0 + lane;
+      const bool ok = c < H / 8;                       // H % 128 == 0: lane pairs are all-or-none
+      const uint4 raw = ok ? src[c] : make_uint4(0, 0, 0, 0);
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      float v[8], amax = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = __uint_as_float(w[q] << 16);
+        v[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+      const float s = nvfp4_scale(amax);
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f16x2 pr = {_Float16(nvfp4_value(v[2 * q], s)), _Float16(nvfp4_value(v[2 * q + 1], s))};
+        o[q] = __builtin_bit_cast(uint32_t, pr);
+      }
+      if (ok) dst[c] = uint4{o[0], o[1], o[2], o[3]};
+    }
+    return;
+  }
   // fp8 codes: lane handles 8 channels -> 8 bytes
   uint2* dst = reinterpret_cast<uint2*>(static_cast<uint8_t*>(outv) + size_t(p) * H);
   for (int c0 = 0; c0 < H / 8; c0 += 64) {              // 512 channels per pass
@@ -185,6 +212,9 @@ hipError_t launch_permute(const moe_config_t& c, const int32_t* topk_idx, const 
         perm_gather<MOE_RECIPE_FP8_B128><<<g, 256, 0, st>>>(x, sorted_pair, pairs, c.top_k, c.hidden, x_perm,
                                                              x_perm_scale);
         break;
+      case MOE_RECIPE_NVFP4:
+        perm_gather<MOE_RECIPE_NVFP4><<<g, 256, 0, st>>>(x, sorted_pair, pairs, c.top_k, c.hidden, x_perm, nullptr);
+        break;
       default:
         perm_gather<MOE_RECIPE_MXFP4><<<g, 256, 0, st>>>(x, sorted_pair, pairs, c.top_k, c.hidden, x_perm,
                                                           x_perm_scale);
@@ -202,6 +232,8 @@ hipError_t launch_quantize_tokens(const moe_config_t& c, const void* x, void* xq
     perm_gather<MOE_RECIPE_FP8_B128><<<g, 256, 0, st>>>(x, nullptr, c.num_tokens, 1, c.hidden, xq, xq_scale);
   else if (c.recipe == MOE_RECIPE_MXFP4)
     perm_gather<MOE_RECIPE_MXFP4><<<g, 256, 0, st>>>(x, nullptr, c.num_tokens, 1, c.hidden, xq, xq_scale);
+  else if (c.recipe == MOE_RECIPE_NVFP4)
+    perm_gather<MOE_RECIPE_NVFP4><<<g, 256, 0, st>>>(x, nullptr, c.num_tokens, 1, c.hidden, xq, nullptr);
   return hipGetLastError();
 }
 

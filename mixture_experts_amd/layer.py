@@ -31,6 +31,9 @@ def alloc_buffers(cfg: _lib.MoeConfig, device="cuda") -> MoELayerBuffers:
     if cfg.recipe in (_lib.RECIPE_F32, _lib.RECIPE_BF16):
         x_perm = torch.empty((P, H), dtype=act, device=device)
         x_perm_scale = None
+    elif cfg.recipe == _lib.RECIPE_NVFP4:                  # fp16 values of the NVFP4 rows
+        x_perm = torch.empty((P, H), dtype=torch.float16, device=device)
+        x_perm_scale = None
     elif cfg.recipe == _lib.RECIPE_FP8_B128:
         x_perm = torch.empty((P, H), dtype=torch.uint8, device=device)
         x_perm_scale = torch.empty((P, H // 128), dtype=torch.float32, device=device)

@@ -58,6 +58,14 @@ reason in the design notes):
      kept in fp32): x = post_attention_layernorm(h) with each row
      (h * r) * weight, r = 1/sqrt(mean(h^2) + eps), evaluated in fp64, rounded to
      fp32 and then to the activation format; out = h + MoE(x).
+  R13 NVFP4 (walk-through section 4: 4-bit floats for routed-expert weights and
+     their input activations, one FP8 scale per 16 values; shared experts stay
+     high precision): per (row, 16 consecutive input channels)
+       s = e4m3(fp32(amax / 6)), taken as 1 when that rounds to 0,
+       q = e2m1(fp32(v / s)) rounding to nearest, ties to even code,
+           saturating at 6 and keeping the sign bit;
+     the value is q * s.  No per-tensor scale (the page names none).  The
+     activations are the rows fed to the routed experts (x and h), as in R7.
 """
 from __future__ import annotations
 
@@ -71,7 +79,7 @@ F64 = np.float64
 SCORE_SIGMOID = 0
 SCORE_SQRTSOFTPLUS = 1
 
-RECIPE_F32, RECIPE_BF16, RECIPE_FP8_B128, RECIPE_MXFP4 = 0, 1, 2, 3
+RECIPE_F32, RECIPE_BF16, RECIPE_FP8_B128, RECIPE_MXFP4, RECIPE_NVFP4 = 0, 1, 2, 3, 4
 
 
 # =============================================================== number formats
@@ -123,6 +131,24 @@ def decode_e2m1_packed(u8: np.ndarray) -> np.ndarray:
     out[..., 0::2] = lo
     out[..., 1::2] = hi
     return out
+
+
+# positive e2m1 values in code order 0..7 and the midpoints between neighbours
+_E2M1_POS = E2M1_TABLE[:8]
+_E2M1_MID = (_E2M1_POS[:-1] + _E2M1_POS[1:]) / 2.0
+
+
+def encode_e2m1(v: np.ndarray) -> np.ndarray:
+    """Round values to e2m1 codes (0..15): nearest, ties to the even code, saturate at 6;
+    the sign bit is kept (a negative value that rounds to zero gives code 8)."""
+    a = np.abs(np.asarray(v, dtype=F64))
+    below = (a[..., None] > _E2M1_MID).sum(axis=-1)            # midpoints strictly below
+    tie = (a[..., None] == _E2M1_MID)
+    # on a tie between codes i and i+1 (midpoint i), take the even one
+    tie_idx = np.where(tie.any(axis=-1), tie.argmax(axis=-1), -1)
+    code = np.where(tie_idx >= 0, np.where(tie_idx % 2 == 0, tie_idx, tie_idx + 1), below)
+    sign = (np.signbit(np.asarray(v, dtype=F64))).astype(np.int64) << 3
+    return (code + sign).astype(np.uint8)
 
 
 def decode_e8m0(u8: np.ndarray) -> np.ndarray:
@@ -285,6 +311,24 @@ def dequant_mxfp8(codes: np.ndarray, e8: np.ndarray) -> np.ndarray:
     return (decode_e4m3(codes).reshape(R, Cn // 32, 32) * decode_e8m0(e8)[:, :, None]).reshape(R, Cn)
 
 
+def quant_nvfp4(v32: np.ndarray):
+    """R13: per (row, 16 channels). Returns (e2m1 codes uint8 [R, C], e4m3 scale codes uint8 [R, C/16])."""
+    R, Cn = v32.shape
+    b = v32.astype(F32).reshape(R, Cn // 16, 16)
+    amax = np.abs(b).max(axis=2)
+    sc = encode_e4m3((amax / F32(6.0)).astype(F32))
+    sc = np.where(decode_e4m3(sc) == 0, encode_e4m3(np.array(1.0)), sc).astype(np.uint8)
+    s = decode_e4m3(sc).astype(F32)
+    q = encode_e2m1((b / s[:, :, None]).astype(F32))
+    return q.reshape(R, Cn), sc
+
+
+def dequant_nvfp4(codes: np.ndarray, scale_codes: np.ndarray) -> np.ndarray:
+    R, Cn = codes.shape
+    return (E2M1_TABLE[codes.astype(np.int64)].reshape(R, Cn // 16, 16)
+            * decode_e4m3(scale_codes)[:, :, None]).reshape(R, Cn)
+
+
 def quantize_rows(recipe: int, v: np.ndarray):
     """Quantise-dequantise rows per the recipe's activation format (identity for f32/bf16)."""
     if recipe == RECIPE_FP8_B128:
@@ -293,6 +337,9 @@ def quantize_rows(recipe: int, v: np.ndarray):
     if recipe == RECIPE_MXFP4:
         q, e = quant_mxfp8(v.astype(F32))
         return dequant_mxfp8(q, e)
+    if recipe == RECIPE_NVFP4:
+        q, s = quant_nvfp4(v.astype(F32))
+        return dequant_nvfp4(q, s)
     return v.astype(F64)
 
 
@@ -301,7 +348,8 @@ def dequant_expert(recipe: int, raw: dict, I: int, H: int):
     """raw: numpy views of one expert's stored weights -> (w13 [2I, H], w2 [H, I]) fp64.
 
     raw keys: w13, w2 (float32 / uint16 bf16 bits / uint8 e4m3 / uint8 packed e2m1),
-              w13_scale, w2_scale (fp32 128x128 block scales or uint8 E8M0 per 32)."""
+              w13_scale, w2_scale (fp32 128x128 block scales, uint8 E8M0 per 32, or
+              uint8 e4m3 per 16 for NVFP4)."""
     if recipe == RECIPE_F32:
         return raw["w13"].astype(F64), raw["w2"].astype(F64)
     if recipe == RECIPE_BF16:
@@ -318,6 +366,12 @@ def dequant_expert(recipe: int, raw: dict, I: int, H: int):
             R, K = v.shape
             return (v.reshape(R, K // 32, 32) * decode_e8m0(e8)[:, :, None]).reshape(R, K)
         return mx(raw["w13"], raw["w13_scale"]), mx(raw["w2"], raw["w2_scale"])
+    if recipe == RECIPE_NVFP4:
+        def nv(q, sc):
+            v = decode_e2m1_packed(q)
+            R, K = v.shape
+            return (v.reshape(R, K // 16, 16) * decode_e4m3(sc)[:, :, None]).reshape(R, K)
+        return nv(raw["w13"], raw["w13_scale"]), nv(raw["w2"], raw["w2_scale"])
     raise ValueError(recipe)
 
 
@@ -362,7 +416,7 @@ def moe_forward(cfg, x64: np.ndarray, gate_w64: np.ndarray, bias32: np.ndarray,
     T, H, k, E = cfg.num_tokens, cfg.hidden, cfg.top_k, cfg.num_experts
     I = cfg.intermediate
     recipe = cfg.recipe
-    quant = recipe in (RECIPE_FP8_B128, RECIPE_MXFP4)
+    quant = recipe in (RECIPE_FP8_B128, RECIPE_MXFP4, RECIPE_NVFP4)
     limit = float(getattr(cfg, "swiglu_limit", 0.0))
     if routing is None:
         routing = route(cfg, x64, gate_w64, bias32)
@@ -421,6 +475,8 @@ def gather_rows(recipe: int, x32: np.ndarray, sorted_pair: np.ndarray, k: int):
         return quant_fp8_b128(rows)
     if recipe == RECIPE_MXFP4:
         return quant_mxfp8(rows)
+    if recipe == RECIPE_NVFP4:                 # stored as the (fp16-exact) values
+        return quantize_rows(RECIPE_NVFP4, rows), None
     return rows, None
 
 

@@ -10,7 +10,10 @@ from oracle import moe_oracle as O
 from workloads import configs as C
 from workloads import generate as G
 
-TOL = {C.RECIPE_F32: 1e-5, C.RECIPE_BF16: 2e-2, C.RECIPE_FP8_B128: 6e-2, C.RECIPE_MXFP4: 6e-2}
+# NVFP4: the same bound as the other quantised recipes (the oracle emulates the
+# quantisation; what remains is fp32 summation order, bf16 outputs and the rare
+# activation code decided differently by those last bits)
+TOL = {C.RECIPE_F32: 1e-5, C.RECIPE_BF16: 2e-2, C.RECIPE_FP8_B128: 6e-2, C.RECIPE_MXFP4: 6e-2, C.RECIPE_NVFP4: 6e-2}
 
 
 def to_np(t: torch.Tensor) -> np.ndarray:

@@ -46,6 +46,8 @@ def _check_x_perm(inp, b, ref):
         assert np.array_equal(got, rows)
     elif cfg.recipe == C.RECIPE_BF16:
         assert np.array_equal(O.decode_bf16(got), rows.astype(np.float64))
+    elif cfg.recipe == C.RECIPE_NVFP4:
+        assert np.array_equal(got.astype(np.float64), rows), f"{(got.astype(np.float64) != rows).sum()} values differ"
     else:
         assert np.array_equal(got, rows), f"{(got != rows).sum()} code bytes differ"
         assert np.array_equal(HN.to_np(b.x_perm_scale), scales)
@@ -150,7 +152,7 @@ def test_edge_cases(kind):
         assert np.all(b.topk_idx.cpu().numpy() == np.arange(k))
 
 
-@pytest.mark.parametrize("cfg", C.FULL_CONFIGS[1:], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", C.FULL_CONFIGS[1:] + C.NEXT_CONFIGS, ids=lambda c: c.name)
 def test_full_size_parity(cfg):
     torch.cuda.empty_cache()
     inp = G.generate(cfg, device="cuda")

@@ -473,3 +473,68 @@ def test_rms_norm_has_unit_rms_and_applies_the_weight_per_channel():
     xe = O.rms_norm(h, np.ones(H), 0.5, O.RECIPE_F32)
     m = (h * h).mean(axis=1)
     np.testing.assert_allclose(xe, h / np.sqrt(m + 0.5)[:, None], rtol=2e-7)
+
+
+# ------------------------------------------------------------------ NVFP4
+def test_encode_e2m1_grid_ties_and_saturation():
+    # every code round-trips (the sign bit of zero included)
+    codes = np.arange(16, dtype=np.uint8)
+    assert np.array_equal(O.encode_e2m1(O.E2M1_TABLE[codes]), codes)
+    # midpoints go to the even code; beyond 6 saturates
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0, 100.0, -0.25, -5.0])
+    assert O.encode_e2m1(mids).tolist() == [0, 2, 2, 4, 4, 6, 6, 7, 7, 8, 14]
+    # nearest on a fine sweep, against a brute-force search over the grid
+    v = np.linspace(-7, 7, 2801)
+    got = O.E2M1_TABLE[O.encode_e2m1(v)]
+    grid = O.E2M1_TABLE[:8]
+    for x, g in zip(v, got):
+        target = min(abs(x), 6.0)
+        assert abs(abs(g) - target) == np.abs(grid - target).min()      # a nearest grid value
+        assert np.sign(g) in (0.0, np.sign(x))
+
+
+def test_nvfp4_quantiser_scale_rule_bounds_and_fp16_exactness():
+    page = json.load(open(os.path.join(HERE, "golden", "page_constants.json")))["nvfp4"]
+    assert page["group_size"] == 16 and page["scale_format"] == "FP8"
+    rng = np.random.default_rng(18)
+    v = (rng.standard_normal((64, 256)) * 10.0 ** rng.uniform(-3, 2, (64, 1))).astype(F32)
+    v[3, 16:32] = 0.0                                   # an all-zero group: scale 1, codes 0
+    v[5, :16] = 0.0; v[5, 7] = 6 * 0.5                  # amax = 6 * 2^-1: the scale is exactly 0.5
+    q, sc = O.quant_nvfp4(v)
+    assert q.shape == v.shape and sc.shape == (64, 256 // page["group_size"])
+    s = O.decode_e4m3(sc)
+    assert s[3, 1] == 1.0 and np.all(q[3, 16:32] % 8 == 0)
+    assert s[5, 0] == 0.5 and O.E2M1_TABLE[q[5, 7]] == 6.0
+    # the scale is the e4m3 value nearest to amax/6
+    amax = np.abs(v.reshape(64, 16, 16)).max(axis=2)
+    nz = amax > 0
+    want = O.decode_e4m3(O.encode_e4m3((amax / F32(6)).astype(F32)))
+    assert np.array_equal(s[nz], np.where(want[nz] == 0, 1.0, want[nz]))
+    dq = O.dequant_nvfp4(q, sc)
+    # error: at most half the e2m1 gap at the value (gaps 0.5, 1, 2), or the clip to 6*s
+    x = np.abs(v.astype(np.float64)) / np.repeat(s, 16, axis=1)
+    gap = np.where(x < 2, 0.5, np.where(x < 4, 1.0, 2.0))
+    err = np.abs(v - dq) / np.repeat(s, 16, axis=1)
+    assert np.all(err <= np.maximum(gap / 2, x - 6.0) + 1e-12)
+    # every dequantised value is exact in fp16 (and bf16): the GPU multiplies them as such
+    assert np.array_equal(dq.astype(np.float16).astype(np.float64), dq)
+    assert np.array_equal(O.decode_bf16(O.encode_bf16(dq.astype(F32))), dq)
+
+
+@pytest.mark.parametrize("recipe", [O.RECIPE_FP8_B128, O.RECIPE_MXFP4, O.RECIPE_NVFP4])
+def test_quantised_recipes_quantise_the_expert_inputs(recipe):
+    """The routed experts see the recipe's quantised activations: the quantiser is
+    idempotent, so feeding already-quantised rows changes no expert output (with the
+    same routing), while a layer that skipped the quantisation would differ."""
+    cfg = {O.RECIPE_FP8_B128: C.MINI_FP8, O.RECIPE_MXFP4: C.MINI_MXFP4, O.RECIPE_NVFP4: C.MINI_NVFP4}[recipe]
+    inp = G.generate(cfg)
+    from tests import harness as HN
+    x = HN.x_f64(inp)
+    gw, b = inp.gate_w.double().numpy(), inp.bias.numpy()
+    s13, s2 = HN.shared_f64(inp)
+    tokens = np.arange(12)
+    r1 = O.moe_forward(cfg, x, gw, b, HN.expert_raw_fn(inp), s13, s2, tokens=tokens)
+    xq = O.quantize_rows(recipe, x.astype(F32))
+    assert np.abs(xq - x).max() > 0                                   # the quantisation is not a no-op
+    r2 = O.moe_forward(cfg, xq, gw, b, HN.expert_raw_fn(inp), s13, s2, tokens=tokens, routing=r1["routing"])
+    np.testing.assert_array_equal(r1["y"], r2["y"])

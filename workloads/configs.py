@@ -21,9 +21,10 @@ RECIPE_F32 = 0          # x, experts, shared, out: fp32
 RECIPE_BF16 = 1         # x, experts, shared, out: bf16
 RECIPE_FP8_B128 = 2     # experts fp8 e4m3fn + fp32 128x128 block scales; activations fp8 per (row,128); shared bf16
 RECIPE_MXFP4 = 3        # experts MXFP4 (e2m1 + E8M0 per 32); activations MXFP8 (e4m3fn + E8M0 per 32); shared bf16
+RECIPE_NVFP4 = 4        # experts and their activations NVFP4 (e2m1 + e4m3 scale per 16); shared bf16
 
 RECIPE_NAMES = {RECIPE_F32: "f32", RECIPE_BF16: "bf16", RECIPE_FP8_B128: "fp8_b128",
-                RECIPE_MXFP4: "mxfp4_mxfp8"}
+                RECIPE_MXFP4: "mxfp4_mxfp8", RECIPE_NVFP4: "nvfp4"}
 
 SCORE_SIGMOID = 0
 SCORE_SQRTSOFTPLUS = 1
@@ -157,10 +158,29 @@ MINI_MIXED_BF16 = MoEConfig(
     description="bf16 mini with a Zipf load: empty experts, 128-row register-streaming tiles and "
                 "256-row LDS tiles in one call, partial column tiles")
 
-MINI_CONFIGS = [MINI_GROUPED_BF16, MINI_DECODE_BF16, MINI_MXFP4, MINI_FP8, MINI_F32, MINI_PREFILL_BF16,
-                MINI_PREFILL_FP8, MINI_MXFP4_WIDE, MINI_MIXED_BF16]
+MINI_NVFP4 = MoEConfig(
+    name="mini_nvfp4", num_tokens=160, hidden=512, num_experts=32, top_k=8,
+    intermediate=256, num_shared=1, shared_intermediate=128,
+    recipe=RECIPE_NVFP4, gate_std=1.0 / 16.0, description="NVFP4 mini (32-to-64-row tiles)")
 
-BY_NAME = {c.name: c for c in FULL_CONFIGS + MINI_CONFIGS}
+MINI_NVFP4_WIDE = MoEConfig(
+    name="mini_nvfp4_wide", num_tokens=560, hidden=384, num_experts=16, top_k=4,
+    intermediate=256, num_shared=1, shared_intermediate=128,
+    recipe=RECIPE_NVFP4, gate_std=1.0 / 16.0,
+    description="NVFP4 mini with about 140 rows per expert: 128-row tiles, partial column tiles")
+
+MINI_CONFIGS = [MINI_GROUPED_BF16, MINI_DECODE_BF16, MINI_MXFP4, MINI_FP8, MINI_F32, MINI_PREFILL_BF16,
+                MINI_PREFILL_FP8, MINI_MXFP4_WIDE, MINI_MIXED_BF16, MINI_NVFP4, MINI_NVFP4_WIDE]
+
+# NVFP4 (walk-through section 4): the decode shape of the Kimi-K2-Thinking-NVFP4 /
+# DeepSeek-V3 layer with NVFP4 routed experts; not one of the five workloads above.
+DECODE_NVFP4 = DECODE_BF16.replace(
+    name="decode_nvfp4", recipe=RECIPE_NVFP4,
+    description="T=128 H=7168 E=384 k=8 I=2048, NVFP4 routed experts and activations, bf16 shared expert")
+
+NEXT_CONFIGS = [DECODE_NVFP4]
+
+BY_NAME = {c.name: c for c in FULL_CONFIGS + MINI_CONFIGS + NEXT_CONFIGS}
 
 
 def get(name: str) -> MoEConfig:

@@ -80,6 +80,25 @@ def encode_e2m1(v: torch.Tensor) -> torch.Tensor:
     return code | sign
 
 
+def encode_nvfp4(w: torch.Tensor):
+    """fp32 [R, K] -> (packed e2m1 uint8 [R, K/2] low nibble = even k, e4m3fn scale codes uint8 [R, K/16]).
+
+    Per 16 consecutive values: scale = e4m3(amax / 6) (1 when that rounds to 0),
+    codes = e2m1(v / scale)."""
+    R, K = w.shape
+    assert K % 16 == 0
+    blk = w.reshape(R, K // 16, 16)
+    amax = blk.abs().amax(dim=2)
+    sc = (amax / E2M1_MAX).to(torch.float8_e4m3fn)
+    s = sc.to(torch.float32)
+    one = torch.ones_like(s)
+    sc = torch.where(s > 0, sc.view(torch.uint8), one.to(torch.float8_e4m3fn).view(torch.uint8))
+    s = torch.where(s > 0, s, one)
+    codes = encode_e2m1(blk / s[:, :, None]).reshape(R, K)
+    packed = codes[:, 0::2] | (codes[:, 1::2] << 4)
+    return packed.contiguous(), sc.contiguous()
+
+
 def encode_mxfp4(w: torch.Tensor):
     """fp32 [R, K] -> (packed e2m1 uint8 [R, K/2] low nibble = even k, E8M0 uint8 [R, K/32]).
 
@@ -187,11 +206,12 @@ def generate(cfg: C.MoEConfig, device="cpu", experts: bool = True) -> MoEInputs:
             w2 = torch.empty((E, H, I), dtype=torch.uint8, device=device)
             w13s = torch.empty((E, 2 * I // 128, H // 128), dtype=torch.float32, device=device)
             w2s = torch.empty((E, H // 128, I // 128), dtype=torch.float32, device=device)
-        elif cfg.recipe == C.RECIPE_MXFP4:
+        elif cfg.recipe in (C.RECIPE_MXFP4, C.RECIPE_NVFP4):
             w13 = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=device)
             w2 = torch.empty((E, H, I // 2), dtype=torch.uint8, device=device)
-            w13s = torch.empty((E, 2 * I, H // 32), dtype=torch.uint8, device=device)
-            w2s = torch.empty((E, H, I // 32), dtype=torch.uint8, device=device)
+            g = 32 if cfg.recipe == C.RECIPE_MXFP4 else 16            # scale group along K
+            w13s = torch.empty((E, 2 * I, H // g), dtype=torch.uint8, device=device)
+            w2s = torch.empty((E, H, I // g), dtype=torch.uint8, device=device)
         for e in range(E):
             a = normal(cfg, "w13", e, (2 * I, H), cfg.expert_std, device)
             b = normal(cfg, "w2", e, (H, I), cfg.expert_std, device)
@@ -201,9 +221,12 @@ def generate(cfg: C.MoEConfig, device="cpu", experts: bool = True) -> MoEInputs:
             elif cfg.recipe == C.RECIPE_FP8_B128:
                 q, s = encode_fp8_block128(a); w13[e].copy_(q); w13s[e].copy_(s)
                 q, s = encode_fp8_block128(b); w2[e].copy_(q); w2s[e].copy_(s)
-            else:
+            elif cfg.recipe == C.RECIPE_MXFP4:
                 q, s = encode_mxfp4(a); w13[e].copy_(q); w13s[e].copy_(s)
                 q, s = encode_mxfp4(b); w2[e].copy_(q); w2s[e].copy_(s)
+            else:
+                q, s = encode_nvfp4(a); w13[e].copy_(q); w13s[e].copy_(s)
+                q, s = encode_nvfp4(b); w2[e].copy_(q); w2s[e].copy_(s)
             del a, b
     sh_dtype = torch.float32 if cfg.recipe == C.RECIPE_F32 else torch.bfloat16
     sw13 = torch.empty((S, 2 * Is, H), dtype=sh_dtype, device=device)
@@ -226,6 +249,8 @@ def expert_weight_bytes(cfg: C.MoEConfig) -> int:
         return 2 * n
     if cfg.recipe == C.RECIPE_FP8_B128:
         return n + 4 * (n // (128 * 128))
+    if cfg.recipe == C.RECIPE_NVFP4:
+        return n // 2 + n // 16
     return n // 2 + n // 32
 
 
