@@ -107,7 +107,8 @@ typedef enum {
  *   n_group > 1 needs at least 2 experts per group;
  *   topk_group * num_experts / n_group >= top_k;
  *   recipes other than F32 need hidden, intermediate and shared_intermediate
- *   to be multiples of 128; F32 needs multiples of 32;
+ *   to be multiples of 128, and MXFP4 and NVFP4 need hidden and intermediate
+ *   to be multiples of 256; F32 needs multiples of 32;
  *   swiglu_limit finite and >= 0.
  * swiglu_limit (the optional SwiGLU truncation of the DeepSeek-V4-Pro overview,
  * FFN entry; the pages give only its name): when > 0, every SwiGLU (routed and

@@ -19,16 +19,26 @@
 //             (one 128x128 scale block); lane half h of sub-step s takes bytes
 //             64h + 32s .. +32; acc += part * a_scale[row] * b_scale[block].
 //   mxfp4     the same MFMA with fp8 activations x fp4 weights and per-32 E8M0
-//             scales on both operands, K = 128 per stage.  Operand layout measured
-//             on gfx950: an fp8 operand lane (half h) holds K = 16h + 0..15 and
-//             32 + 16h + 0..15, an fp4 operand lane holds K = 32h + 0..31 (even K in
-//             the low nibble), and the scale of lane (row, h) applies to K block h.
-//   nvfp4     v_mfma_f32_32x32x16_f16 on exactly dequantised operands: activations
-//             arrive as the fp16 values of their NVFP4 quantisation; e2m1 weights
-//             are turned into fp16 in registers (byte lookup of the fp16 high byte,
-//             times the group's e4m3 scale: every such product is exact in fp16).
+//             scales on both operands, K = 256 per stage (128 weight bytes per
+//             row: one full cache line).  Operand layout measured on gfx950: an
+//             fp8 operand lane (half h) holds K = 16h + 0..15 and 32 + 16h + 0..15,
+//             an fp4 operand lane holds K = 32h + 0..31 (even K in the low
+//             nibble), and the scale of lane (row, h) applies to K block h.  MFMA
+//             m of a stage gives weight lane half h the stage's K 128h + 32m .. +32.
+//   nvfp4     v_mfma_f32_32x32x16_f16 on exactly dequantised operands, K = 256 per
+//             stage: activations arrive as the fp16 values of their NVFP4
+//             quantisation; e2m1 weights are turned into fp16 in registers (byte
+//             lookup of the fp16 high byte, times the group's e4m3 scale: every
+//             such product is exact in fp16).  Step s gives lane half h the
+//             stage's K 128h + 8s .. +8.
+// The fp4 stages are twice (MX) or four times (NVFP4) as deep as the bf16 one so
+// that every stage still reads whole 128-byte lines of each weight row: a stage
+// that reads part of a line leaves the rest to a later stage, by when the line
+// has left L2 and is fetched again.
 // The SwiGLU output h is written as bf16, or re-quantised to the activation format
 // (NVFP4: stored as fp16 values).
+#include <type_traits>
+
 #include "gemm_common.h"
 #include "kernels.h"
 
@@ -36,13 +46,19 @@ namespace moe {
 
 namespace {
 
-constexpr int RS_ROWB = 128;     // activation bytes of K per LDS row and stage
+constexpr int RS_ROWB = 128;     // bf16 / fp8: activation bytes of K per LDS row and stage
 constexpr int RS_NB = 256;       // weight rows per tile
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__device__ __forceinline__ int rs_slot(int r, int c) { return c ^ ((r ^ (r >> 1)) & 7); }
-__device__ __forceinline__ int rs_swz(int r, int c) { return r * RS_ROWB + (rs_slot(r, c) << 4); }
+// Slot of logical 16-byte chunk c in an LDS row r of ROWB bytes: rows of 128 bytes
+// share a bank line in pairs; longer rows start every bank line afresh.
+template <int ROWB>
+__device__ __forceinline__ int rs_slot(int r, int c) {
+  return ROWB == 128 ? c ^ ((r ^ (r >> 1)) & 7) : c ^ (r & 15);
+}
+template <int ROWB>
+__device__ __forceinline__ int rs_swz(int r, int c) { return r * ROWB + (rs_slot<ROWB>(r, c) << 4); }
 
 template <int N>
 __device__ __forceinline__ void rs_wait_vmcnt() {
@@ -50,28 +66,45 @@ __device__ __forceinline__ void rs_wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
 }
 
+// Workgroup barrier that leaves the weight loads into registers in flight.  A
+// fenced barrier (__syncthreads(), or a release fence on LDS alone while async
+// LDS copies are outstanding) waits for every vector memory operation of the
+// wave.  Here the stage's own async copies are waited for explicitly (vmcnt)
+// before the barrier, LDS reads and writes (lgkmcnt) in the same asm; the
+// "memory" clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void rs_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ void rs_copy16(const void* g, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_wave_base, 16, 0, 0);
 }
 
-// Eight e2m1 codes (one dword, low nibble = lower k) times an fp16 scale pair ->
-// eight fp16 values in k order.  The magnitudes index a byte table of the fp16
-// high bytes (the low byte of every e2m1 value in fp16 is zero); the sign bit of
-// each nibble becomes the fp16 sign.
-__device__ __forceinline__ f16x8 e2m1x8_to_f16(uint32_t w, f16x2 scale) {
-  constexpr uint32_t T_LO = 0x3E3C3800u, T_HI = 0x46444240u;   // 0, .5, 1, 1.5 | 2, 3, 4, 6
-  const uint32_t he = __builtin_amdgcn_perm(T_HI, T_LO, w & 0x07070707u) | ((w << 4) & 0x80808080u);   // even k
-  const uint32_t ho = __builtin_amdgcn_perm(T_HI, T_LO, (w >> 4) & 0x07070707u) | (w & 0x80808080u);   // odd k
-  f16x8 out;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    // bytes: 0, even k = 2q high byte, 0, odd k = 2q+1 high byte
-    const uint32_t d = __builtin_amdgcn_perm(ho, he, 0x040C000Cu + 0x01000100u * q);
-    const f16x2 v = __builtin_bit_cast(f16x2, d) * scale;
-    out[2 * q] = v[0];
-    out[2 * q + 1] = v[1];
-  }
-  return out;
+// An NVFP4 group scale (e4m3 code) split as s = 2^e * m for the dequantisation
+// below: the f32 value s (whose exponent is 2^e) and m = s / 2^e in fp16, at most
+// four significant bits, the sign of s included.
+struct NvScale {
+  float s;
+  f16x2 m;
+};
+__device__ __forceinline__ NvScale nv_scale(uint32_t code) {
+  // e4m3 -> fp16 without a branch: the code's exponent and mantissa bits placed
+  // as an fp16 pattern read 2^-8 times the value (e4m3 subnormals become fp16
+  // subnormals), and 2^8 times that is exact
+  const uint32_t hb = ((code & 0x7Fu) << 7) | ((code & 0x80u) << 8);
+  const _Float16 h = __builtin_bit_cast(_Float16, uint16_t(hb)) * _Float16(256.0f);
+  const uint32_t mh = (uint32_t(__builtin_bit_cast(uint16_t, h)) & 0x83FFu) | 0x3C00u;
+  return NvScale{float(h), __builtin_bit_cast(f16x2, mh | (mh << 16))};
+}
+
+// Eight e2m1 codes (one dword, low nibble = lower k) times a group scale -> eight
+// fp16 values in k order.  The fp4 conversion applies 2^e (it takes only the
+// exponent of its f32 scale operand), one packed multiply per pair applies m; the
+// e2m1 value times 2^e and then times m are exact in fp16.
+__device__ __forceinline__ f16x8 e2m1x8_to_f16(uint32_t w, NvScale sc) {
+  const f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc.s, 0) * sc.m;
+  const f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc.s, 1) * sc.m;
+  const f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc.s, 2) * sc.m;
+  const f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc.s, 3) * sc.m;
+  return f16x8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
 }
 
 __device__ __forceinline__ i32x8 rs_cat(uint4 lo, uint4 hi) {
@@ -91,14 +124,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   constexpr bool FP4 = MX || NV;                   // packed e2m1 weights with per-row scale bytes
   constexpr bool ASC = FP8 || MX;                  // activations as codes plus row scales
   constexpr int EA = (BF16 || NV) ? 2 : 1;         // activation bytes per element (NVFP4: fp16 values)
-  constexpr int KS = RS_ROWB / EA;                 // K per stage
-  constexpr int WB = FP4 ? 2 : 1;                  // weight elements per byte (fp4: 2)
-  constexpr int EBW = BF16 ? 2 : 1;                // weight bytes per element (bf16 2, fp8 1; fp4 via WB)
-  constexpr int BCH = MX ? 2 : (NV ? 1 : 4);       // 16-byte weight chunks per fragment and stage
+  constexpr int KS = FP4 ? 256 : RS_ROWB / EA;     // K per stage: 128 weight bytes of every row
+  constexpr int AROWB = KS * EA;                   // activation bytes per LDS row and stage
+  constexpr int CPR = AROWB / 16;                  // 16-byte chunks per LDS row
+  constexpr int EBW = BF16 ? 2 : 1;                // weight bytes per element (bf16 2, fp8 1; fp4 half)
+  constexpr int BCH = 4;                           // 16-byte weight chunks per lane, fragment and stage
   constexpr int SG = MX ? 32 : 16;                 // fp4 scale group along K
-  constexpr int A_INSTR = MS;                      // async copies per wave per stage: BM*8 chunks / 256 lanes
-  __shared__ __attribute__((aligned(1024))) uint8_t As[NST][BM * RS_ROWB];
-  __shared__ uint32_t Sa[NST][BM];                 // fp8: fp32 row scale bits; MX: 4 E8M0 bytes
+  constexpr int A_INSTR = MS * CPR / 8;            // async copies per wave per stage: BM*CPR chunks / 256 lanes
+  // per-row activation scales of a stage (fp8: fp32 bits of one scale; MX: 8 E8M0
+  // bytes) and a lane's weight scales of a stage (MX: 4 E8M0 bytes; NVFP4: 8 e4m3)
+  using SaT = std::conditional_t<MX, uint2, uint32_t>;
+  using SbT = std::conditional_t<NV, uint2, uint32_t>;
+  static_assert(size_t(NST) * BM * (AROWB + sizeof(SaT)) + 4 * BM * 4 <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) uint8_t As[NST][BM * AROWB];
+  __shared__ SaT Sa[NST][BM];
   __shared__ float amax_lds[4][BM];
 
   // (row tile, column block) pairs in XCD-major order: one expert's row tiles and
@@ -150,11 +189,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     const size_t sub_stride = FP4 ? size_t(g.N) * ns / 2 : size_t(g.N) * ns * EBW;
     return size_t(k0 / ns) * sub_stride + (FP4 ? size_t(k0 % ns) / 2 : size_t(k0 % ns) * EBW);
   };
-  // this lane's weight bytes for the stage at k0, per fragment: bf16 and fp8 64
-  // contiguous bytes at 64h; MX two 16-byte pieces at 32s + 16h
-  auto bsrc = [&](int f, int k0) -> const uint8_t* {
-    return brow[f] + koff(k0) + (FP4 ? half * 16 : half * 64);
-  };
+  // this lane's weight bytes for the stage at k0, per fragment: the 64 contiguous
+  // bytes at 64h of the row's 128
+  auto bsrc = [&](int f, int k0) -> const uint8_t* { return brow[f] + koff(k0) + half * 64; };
   auto bscale_fp8 = [&](int f, int k0) -> float {
     const float* S = static_cast<const float*>(g.B_scale);
     if (MODE == EPI_SWIGLU) {
@@ -165,33 +202,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     const int cb = min(n0 + wave * 64 + f * 32, g.N - 1) / 128;
     return S[(size_t(sub) * (g.N / 128) + cb) * (ns / 128) + (k0 % ns) / 128];
   };
-  // fp4 weight scales of fragment f at k0: 4 scale bytes (groups k0/SG .. +3) of this
-  // lane's row: MX E8M0 per 32, NVFP4 e4m3 codes per 16
-  auto bscale_fp4 = [&](int f, int k0) -> uint32_t {
+  // fp4 weight scales of fragment f at k0 for this lane's half of the stage: MX
+  // E8M0 per 32 (groups k0/32 + 4h .. +3), NVFP4 e4m3 per 16 (k0/16 + 8h .. +7)
+  auto bscale_fp4 = [&](int f, int k0) -> SbT {
     const uint8_t* S = static_cast<const uint8_t*>(g.B_scale);
-    if (MODE == EPI_SWIGLU)
-      return *reinterpret_cast<const uint32_t*>(S + (size_t(sub0) * 2 * ns + ncol[f]) * (K / SG) + k0 / SG);
-    const int sub = ti.e * g.n_experts_split + k0 / ns;
-    return *reinterpret_cast<const uint32_t*>(S + (size_t(sub) * g.N + ncol[f]) * (ns / SG) + (k0 % ns) / SG);
+    const uint8_t* p;
+    if (MODE == EPI_SWIGLU) {
+      p = S + (size_t(sub0) * 2 * ns + ncol[f]) * (K / SG) + k0 / SG;
+    } else {
+      const int sub = ti.e * g.n_experts_split + k0 / ns;
+      p = S + (size_t(sub) * g.N + ncol[f]) * (ns / SG) + (k0 % ns) / SG;
+    }
+    return *reinterpret_cast<const SbT*>(p + half * (KS / SG / 2));
   };
 
   // ---- activation copies: copy j of wave w fills LDS chunk positions (w*MS + j)*64 + lane
   const uint8_t* a_src[A_INSTR];
 #pragma unroll
   for (int j = 0; j < A_INSTR; ++j) {
-    const int p = (wave * A_INSTR + j) * 64 + lane, r = p >> 3, c = rs_slot(r, p & 7);
+    const int p = (wave * A_INSTR + j) * 64 + lane, r = p / CPR, c = rs_slot<AROWB>(r, p % CPR);
     a_src[j] = A + size_t(a_row(g, ti.row0 + min(r, ti.rows - 1))) * g.lda * EA + c * 16;
   }
   const int sa_row = ASC ? a_row(g, ti.row0 + min(tid % BM, ti.rows - 1)) : 0;
-  auto load_sa = [&](int k0) -> uint32_t {        // every thread loads (rows clamped): equal vmcnt per wave
-    if (MX) return *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(g.A_scale) +
-                                                      size_t(sa_row) * (K / 32) + k0 / 32);
-    return __float_as_uint(static_cast<const float*>(g.A_scale)[size_t(sa_row) * (K / 128) + k0 / 128]);
+  auto load_sa = [&](int k0) -> SaT {            // every thread loads (rows clamped): equal vmcnt per wave
+    if constexpr (MX)
+      return *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(g.A_scale) + size_t(sa_row) * (K / 32) + k0 / 32);
+    else
+      return __float_as_uint(static_cast<const float*>(g.A_scale)[size_t(sa_row) * (K / 128) + k0 / 128]);
   };
 
   uint4 breg[NST][2][BCH];
-  uint32_t sreg[NST];
-  uint32_t sbm[NST][2];
+  SaT sreg[NST];
+  SbT sbm[NST][2];
   auto issue = [&](int k0, int buf) {
 #pragma unroll
     for (int j = 0; j < A_INSTR; ++j)
@@ -203,7 +245,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     for (int f = 0; f < 2; ++f) {
       const uint8_t* p = bsrc(f, k0);
 #pragma unroll
-      for (int c = 0; c < BCH; ++c) breg[buf][f][c] = *reinterpret_cast<const uint4*>(p + c * (MX ? 32 : 16));
+      for (int c = 0; c < BCH; ++c) breg[buf][f][c] = *reinterpret_cast<const uint4*>(p + c * 16);
       if (FP4) sbm[buf][f] = bscale_fp4(f, k0);
     }
   };
@@ -220,9 +262,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   // this block's K stages (a K split only in the plain store mode)
   const int nz = (MODE == EPI_STORE) ? int(gridDim.z) : 1;
   const int KT = K / KS / nz, kb = (MODE == EPI_STORE) ? int(blockIdx.z) * KT : 0;
+  // fp4 rings keep their weight loads in flight across the stage barrier
+  // (rs_barrier), and rings of three or more stages, and MXFP4's gate/up ring,
+  // issue one stage in every iteration (past the end: the last stage again, an L2
+  // hit): each wave then always has NST-1 stages in flight and one wait count that
+  // the compiler can track covers every iteration.  Otherwise only real stages
+  // are issued (a surplus stage holds up the epilogue, which costs a short K loop
+  // most), and bf16 and fp8 take a plain __syncthreads() (measured: as fast or
+  // faster for them).
+  constexpr bool EVERY = FP4 && (NST >= 3 || (MX && MODE == EPI_SWIGLU));
 #pragma unroll
-  for (int s = 0; s < NST - 1; ++s)
-    if (s < KT) issue((kb + s) * KS, s);
+  for (int s = 0; s < NST - 1; ++s) {
+    if (EVERY) issue((kb + min(s, KT - 1)) * KS, s);
+    else if (s < KT) issue((kb + s) * KS, s);
+  }
 
   for (int kt0 = 0; kt0 < KT; kt0 += NST) {
 #pragma unroll
@@ -231,56 +284,65 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
       if (kt >= KT) break;
       // stage kt's activation copies must have landed in every wave's LDS slots;
       // the weight registers are waited for by the compiler at their first use
-      if (NST >= 3 && kt + 1 < KT) rs_wait_vmcnt<(NST >= 3 ? (NST - 2) * PER_STAGE : 0)>();
+      if (EVERY || (NST >= 3 && kt + 1 < KT)) rs_wait_vmcnt<(NST >= 3 ? (NST - 2) * PER_STAGE : 0)>();
       else rs_wait_vmcnt<0>();
-      if (!BF16 && tid < BM) Sa[buf][tid] = sreg[buf];
-      __syncthreads();
+      if (ASC && tid < BM) Sa[buf][tid] = sreg[buf];
+      if constexpr (FP4) rs_barrier();
+      else __syncthreads();
       const int nb = (buf + NST - 1) % NST;
-      if (kt + NST - 1 < KT) issue((kb + kt + NST - 1) * KS, nb);
-      if (!wave_on) continue;
+      if (EVERY) {
+        issue((kb + min(kt + NST - 1, KT - 1)) * KS, nb);
+        __builtin_amdgcn_sched_barrier(0);         // the next stage's loads go out before this one's compute
+      } else if (kt + NST - 1 < KT) {
+        issue((kb + kt + NST - 1) * KS, nb);
+      }
+      // (fp4: a wave without columns computes on its clamped rows and stores
+      // nothing, with no branch around the accumulators)
+      if (!FP4 && !wave_on) continue;
       const uint8_t* Ab = As[buf];
-      if (BF16) {
+      if constexpr (BF16) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const bf16x8 b0 = __builtin_bit_cast(bf16x8, breg[buf][0][s]);
           const bf16x8 b1 = __builtin_bit_cast(bf16x8, breg[buf][1][s]);
 #pragma unroll
           for (int i = 0; i < MS; ++i) {
-            if (i < act_ms) {
+            if ((NV && MS == 1 && i == 0) || i < act_ms) {   // (one row block: always holds rows)
               const bf16x8 a =
-                  __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Ab + rs_swz(i * 32 + l32, half * 4 + s)));
+                  __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Ab + rs_swz<AROWB>(i * 32 + l32, half * 4 + s)));
               acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[i][0], 0, 0, 0);
               acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[i][1], 0, 0, 0);
             }
           }
         }
-      } else if (NV) {
+      } else if constexpr (NV) {
         // fp16 MFMA on exactly dequantised operands: the activations are fp16 values
         // already; the weights' e2m1 codes become fp16 by a byte lookup, times the
-        // group's e4m3 scale (every product is exact in fp16).  Lane half h, step s
-        // takes k = 32h + 8s .. +8 on both sides: step s uses dword s of the lane's
-        // 16 weight bytes and scale byte 2h + s/2 of the stage's four.
+        // group's e4m3 scale (every product is exact in fp16).  Step s takes the
+        // stage's k = 128h + 8s .. +8 in lane half h on both sides: dword s of the
+        // lane's 64 weight bytes, scale byte s/2 of its eight, activation chunk
+        // 16h + s of the row.
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < 16; ++s) {
           f16x8 bw[2];
 #pragma unroll
           for (int f = 0; f < 2; ++f) {
-            const uint32_t w = (s == 0) ? breg[buf][f][0].x : (s == 1) ? breg[buf][f][0].y
-                             : (s == 2) ? breg[buf][f][0].z : breg[buf][f][0].w;
-            const _Float16 sc = _Float16(e4m3_to_f32((sbm[buf][f] >> (8 * (2 * half + (s >> 1)))) & 0xffu));
-            bw[f] = e2m1x8_to_f16(w, f16x2{sc, sc});
+            const uint4 q = breg[buf][f][s >> 2];
+            const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
+            const uint32_t sw = (s >> 3) ? sbm[buf][f].y : sbm[buf][f].x;
+            bw[f] = e2m1x8_to_f16(w, nv_scale((sw >> (8 * ((s >> 1) & 3))) & 0xffu));
           }
 #pragma unroll
           for (int i = 0; i < MS; ++i) {
-            if (i < act_ms) {
-              const f16x8 a =
-                  __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(Ab + rs_swz(i * 32 + l32, half * 4 + s)));
+            if ((NV && MS == 1 && i == 0) || i < act_ms) {
+              const f16x8 a = __builtin_bit_cast(
+                  f16x8, *reinterpret_cast<const uint4*>(Ab + rs_swz<AROWB>(i * 32 + l32, 16 * half + s)));
               acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bw[0], a, acc[i][0], 0, 0, 0);
               acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bw[1], a, acc[i][1], 0, 0, 0);
             }
           }
         }
-      } else if (FP8) {
+      } else if constexpr (FP8) {
         const float sb0 = bscale_fp8(0, (kb + kt) * KS), sb1 = bscale_fp8(1, (kb + kt) * KS);
 #pragma unroll
         for (int i = 0; i < MS; ++i) {
@@ -289,8 +351,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
           i32x8 a[2];
 #pragma unroll
           for (int s = 0; s < 2; ++s)
-            a[s] = rs_cat(*reinterpret_cast<const uint4*>(Ab + rs_swz(ar, 4 * half + 2 * s)),
-                          *reinterpret_cast<const uint4*>(Ab + rs_swz(ar, 4 * half + 2 * s + 1)));
+            a[s] = rs_cat(*reinterpret_cast<const uint4*>(Ab + rs_swz<AROWB>(ar, 4 * half + 2 * s)),
+                          *reinterpret_cast<const uint4*>(Ab + rs_swz<AROWB>(ar, 4 * half + 2 * s + 1)));
           const float ra = __uint_as_float(Sa[buf][ar]);   // this lane's token row
 #pragma unroll
           for (int f = 0; f < 2; ++f) {
@@ -307,24 +369,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
           }
         }
       } else {  // MX
+        // MFMA m: weight lane half h holds the stage's K 128h + 32m .. +32 (window
+        // block h); the fp8 operand lane half h the matching K 32m + 16h .. +16
+        // (chunk 2m + h) and 128 + 32m + 16h .. +16 (chunk 8 + 2m + h); both scales
+        // of lane (row, h) are group 4h + m of the stage.
 #pragma unroll
         for (int i = 0; i < MS; ++i) {
           if (i >= act_ms) continue;
           const int ar = i * 32 + l32;
-          const uint32_t sa4 = Sa[buf][ar];
+          const uint2 sa8 = Sa[buf][ar];
+          const uint32_t saw = half ? sa8.y : sa8.x;
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            // K 64s + 16h .. +16 and 64s + 32 + 16h .. +16 of the stage
-            const i32x8 a = rs_cat(*reinterpret_cast<const uint4*>(Ab + rs_swz(ar, 4 * s + half)),
-                                   *reinterpret_cast<const uint4*>(Ab + rs_swz(ar, 4 * s + 2 + half)));
-            const int sh = 8 * (2 * s + half);
-            const int sa = int((sa4 >> sh) & 0xffu);
+          for (int m = 0; m < 4; ++m) {
+            const i32x8 a = rs_cat(*reinterpret_cast<const uint4*>(Ab + rs_swz<AROWB>(ar, 2 * m + half)),
+                                   *reinterpret_cast<const uint4*>(Ab + rs_swz<AROWB>(ar, 8 + 2 * m + half)));
+            const int sa = int((saw >> (8 * m)) & 0xffu);
 #pragma unroll
             for (int f = 0; f < 2; ++f) {
-              const uint4 bw = breg[buf][f][s];
+              const uint4 bw = breg[buf][f][m];
               const i32x8 b = i32x8{int(bw.x), int(bw.y), int(bw.z), int(bw.w), 0, 0, 0, 0};
               acc[i][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  b, a, acc[i][f], 4, 0, 0, int((sbm[buf][f] >> sh) & 0xffu), 0, sa);
+                  b, a, acc[i][f], 4, 0, 0, int((sbm[buf][f] >> (8 * m)) & 0xffu), 0, sa);
             }
           }
         }
@@ -499,8 +564,8 @@ static void rs_launch(int ms, dim3 grid, const GemmArgs& g, hipStream_t st) {
       return;
     }
   }
-  // NVFP4 moves 0.56 weight bytes per element: a deeper ring keeps enough of them in flight
-  if (ms <= 1) ffn_rs_kernel<1, MODE, RECIPE, (RECIPE == MOE_RECIPE_NVFP4 ? 6 : RS_NST1)><<<grid, 256, 0, st>>>(g);
+  // NVFP4's stages carry fp16 activations four times as deep as bf16's: one more stage in flight
+  if (ms <= 1) ffn_rs_kernel<1, MODE, RECIPE, (RECIPE == MOE_RECIPE_NVFP4 ? 3 : RS_NST1)><<<grid, 256, 0, st>>>(g);
   else ffn_rs_kernel<2, MODE, RECIPE, RS_NST2, (RECIPE == MOE_RECIPE_FP8_B128 ? 2 : 1)><<<grid, 256, 0, st>>>(g);
 }
 

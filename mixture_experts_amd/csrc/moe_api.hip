@@ -43,7 +43,10 @@ bool valid_config(const moe_config_t* c) {
 
 bool supported_shape(const moe_config_t* c) {
   const int q = (c->recipe == MOE_RECIPE_F32) ? 32 : 128;
-  if (c->hidden % q || c->intermediate % q) return false;
+  // the fp4 routed GEMMs take 256 K per stage (one 128-byte line of every weight row)
+  const bool fp4 = c->recipe == MOE_RECIPE_MXFP4 || c->recipe == MOE_RECIPE_NVFP4;
+  const int qr = fp4 ? 256 : q;
+  if (c->hidden % qr || c->intermediate % qr) return false;
   if (c->num_shared > 0 && c->shared_intermediate % q) return false;
   return true;
 }

@@ -73,8 +73,13 @@ def test_invalid_configs_are_rejected_without_launch(bad):
     assert st == 1  # MOE_ERR_INVALID_ARGUMENT
 
 
-def test_unsupported_shapes_report_unsupported():
-    cfg = M.make_config(C.DECODE_BF16.replace(hidden=7100))
+@pytest.mark.parametrize("base,change", [
+    (C.DECODE_BF16, dict(hidden=7100)),
+    (C.MINI_MXFP4, dict(hidden=384)),          # fp4 recipes: multiples of 256
+    (C.MINI_NVFP4, dict(intermediate=384)),
+], ids=["bf16-hidden-7100", "mxfp4-hidden-384", "nvfp4-intermediate-384"])
+def test_unsupported_shapes_report_unsupported(base, change):
+    cfg = M.make_config(base.replace(**change))
     assert M.moe_workspace_bytes(cfg) == 0
     st = M.load().moe_forward(ctypes.byref(cfg), None, None, None, None, None, None, None, None, None, 0, None)
     assert st == 2  # MOE_ERR_UNSUPPORTED

@@ -146,7 +146,7 @@ MINI_PREFILL_FP8 = MoEConfig(
     gate_std=1.0 / 16.0, description="prefill-shaped fp8 mini: 128-row tiles")
 
 MINI_MXFP4_WIDE = MoEConfig(
-    name="mini_mxfp4_wide", num_tokens=560, hidden=384, num_experts=16, top_k=4,
+    name="mini_mxfp4_wide", num_tokens=560, hidden=512, num_experts=16, top_k=4,
     intermediate=256, num_shared=1, shared_intermediate=128,
     recipe=RECIPE_MXFP4, gate_std=1.0 / 16.0,
     description="MXFP4 mini with about 140 rows per expert: two or three ragged row tiles per expert")
@@ -164,10 +164,10 @@ MINI_NVFP4 = MoEConfig(
     recipe=RECIPE_NVFP4, gate_std=1.0 / 16.0, description="NVFP4 mini (32-to-64-row tiles)")
 
 MINI_NVFP4_WIDE = MoEConfig(
-    name="mini_nvfp4_wide", num_tokens=560, hidden=384, num_experts=16, top_k=4,
+    name="mini_nvfp4_wide", num_tokens=560, hidden=512, num_experts=16, top_k=4,
     intermediate=256, num_shared=1, shared_intermediate=128,
     recipe=RECIPE_NVFP4, gate_std=1.0 / 16.0,
-    description="NVFP4 mini with about 140 rows per expert: 128-row tiles, partial column tiles")
+    description="NVFP4 mini with about 140 rows per expert: 128-row tiles")
 
 MINI_CONFIGS = [MINI_GROUPED_BF16, MINI_DECODE_BF16, MINI_MXFP4, MINI_FP8, MINI_F32, MINI_PREFILL_BF16,
                 MINI_PREFILL_FP8, MINI_MXFP4_WIDE, MINI_MIXED_BF16, MINI_NVFP4, MINI_NVFP4_WIDE]
