@@ -7,7 +7,8 @@
 // up_proj rows; down: 256 output columns); four wavefronts, wave w owns every row
 // and weight rows [32w, 32w+32) of each half.  Weights go straight from HBM into
 // MFMA B-operand registers through a ring of NST register stages (NST-1 stages in
-// flight per wave), each lane reading 64 contiguous bytes per fragment and stage;
+// flight per wave), each lane reading its half of the row's 128 bytes per stage
+// (MXFP4 down GEMM: 64) as contiguous 16-byte loads;
 // the few activation rows go through a matching LDS ring filled by async
 // global->LDS copies.  Small register footprint -> several waves per SIMD, so
 // plenty of weight bytes are in flight per CU.
@@ -20,11 +21,12 @@
 //             64h + 32s .. +32; acc += part * a_scale[row] * b_scale[block].
 //   mxfp4     the same MFMA with fp8 activations x fp4 weights and per-32 E8M0
 //             scales on both operands, K = 256 per stage (128 weight bytes per
-//             row: one full cache line).  Operand layout measured on gfx950: an
+//             row: one full cache line); 128 in the down GEMM.  Operand layout measured on gfx950: an
 //             fp8 operand lane (half h) holds K = 16h + 0..15 and 32 + 16h + 0..15,
 //             an fp4 operand lane holds K = 32h + 0..31 (even K in the low
 //             nibble), and the scale of lane (row, h) applies to K block h.  MFMA
-//             m of a stage gives weight lane half h the stage's K 128h + 32m .. +32.
+//             m of a stage gives weight lane half h the stage's K (KS/2)h + 32m
+//             .. +32.
 //   nvfp4     v_mfma_f32_32x32x16_f16 on exactly dequantised operands, K = 256 per
 //             stage: activations arrive as the fp16 values of their NVFP4
 //             quantisation; e2m1 weights are turned into fp16 in registers (byte
@@ -124,17 +126,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   constexpr bool FP4 = MX || NV;                   // packed e2m1 weights with per-row scale bytes
   constexpr bool ASC = FP8 || MX;                  // activations as codes plus row scales
   constexpr int EA = (BF16 || NV) ? 2 : 1;         // activation bytes per element (NVFP4: fp16 values)
-  constexpr int KS = FP4 ? 256 : RS_ROWB / EA;     // K per stage: 128 weight bytes of every row
+  // K per stage: 128 weight bytes of every row, except MXFP4's down GEMM (K =
+  // intermediate, a short loop), whose two-stage ring pays one stage's load and
+  // one stage's compute per tile without overlap: 128-deep stages halve both
+  constexpr int KS = FP4 ? ((MX && MODE == EPI_STORE) ? 128 : 256) : RS_ROWB / EA;
   constexpr int AROWB = KS * EA;                   // activation bytes per LDS row and stage
   constexpr int CPR = AROWB / 16;                  // 16-byte chunks per LDS row
   constexpr int EBW = BF16 ? 2 : 1;                // weight bytes per element (bf16 2, fp8 1; fp4 half)
-  constexpr int BCH = 4;                           // 16-byte weight chunks per lane, fragment and stage
+  constexpr int WROWB = FP4 ? KS / 2 : KS * EBW;   // weight bytes per row and stage
+  constexpr int BCH = WROWB / 32;                  // 16-byte weight chunks per lane, fragment and stage
   constexpr int SG = MX ? 32 : 16;                 // fp4 scale group along K
   constexpr int A_INSTR = MS * CPR / 8;            // async copies per wave per stage: BM*CPR chunks / 256 lanes
-  // per-row activation scales of a stage (fp8: fp32 bits of one scale; MX: 8 E8M0
-  // bytes) and a lane's weight scales of a stage (MX: 4 E8M0 bytes; NVFP4: 8 e4m3)
-  using SaT = std::conditional_t<MX, uint2, uint32_t>;
-  using SbT = std::conditional_t<NV, uint2, uint32_t>;
+  // per-row activation scales of a stage (fp8: fp32 bits of one scale; MX: KS/32
+  // E8M0 bytes) and a lane's weight scales of a stage (its half: MX KS/64 E8M0
+  // bytes; NVFP4 8 e4m3 bytes)
+  using SaT = std::conditional_t<MX && KS == 256, uint2, uint32_t>;
+  using SbT = std::conditional_t<NV, uint2, std::conditional_t<KS == 256, uint32_t, uint16_t>>;
   static_assert(size_t(NST) * BM * (AROWB + sizeof(SaT)) + 4 * BM * 4 <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) uint8_t As[NST][BM * AROWB];
   __shared__ SaT Sa[NST][BM];
@@ -189,9 +196,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     const size_t sub_stride = FP4 ? size_t(g.N) * ns / 2 : size_t(g.N) * ns * EBW;
     return size_t(k0 / ns) * sub_stride + (FP4 ? size_t(k0 % ns) / 2 : size_t(k0 % ns) * EBW);
   };
-  // this lane's weight bytes for the stage at k0, per fragment: the 64 contiguous
-  // bytes at 64h of the row's 128
-  auto bsrc = [&](int f, int k0) -> const uint8_t* { return brow[f] + koff(k0) + half * 64; };
+  // this lane's weight bytes for the stage at k0, per fragment: its half of the
+  // row's WROWB contiguous bytes
+  auto bsrc = [&](int f, int k0) -> const uint8_t* { return brow[f] + koff(k0) + half * (WROWB / 2); };
   auto bscale_fp8 = [&](int f, int k0) -> float {
     const float* S = static_cast<const float*>(g.B_scale);
     if (MODE == EPI_SWIGLU) {
@@ -203,7 +210,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     return S[(size_t(sub) * (g.N / 128) + cb) * (ns / 128) + (k0 % ns) / 128];
   };
   // fp4 weight scales of fragment f at k0 for this lane's half of the stage: MX
-  // E8M0 per 32 (groups k0/32 + 4h .. +3), NVFP4 e4m3 per 16 (k0/16 + 8h .. +7)
+  // E8M0 per 32 (groups k0/32 + (KS/64)h ..), NVFP4 e4m3 per 16 (k0/16 + 8h .. +7)
   auto bscale_fp4 = [&](int f, int k0) -> SbT {
     const uint8_t* S = static_cast<const uint8_t*>(g.B_scale);
     const uint8_t* p;
@@ -226,7 +233,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   const int sa_row = ASC ? a_row(g, ti.row0 + min(tid % BM, ti.rows - 1)) : 0;
   auto load_sa = [&](int k0) -> SaT {            // every thread loads (rows clamped): equal vmcnt per wave
     if constexpr (MX)
-      return *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(g.A_scale) + size_t(sa_row) * (K / 32) + k0 / 32);
+      return *reinterpret_cast<const SaT*>(static_cast<const uint8_t*>(g.A_scale) + size_t(sa_row) * (K / 32) + k0 / 32);
     else
       return __float_as_uint(static_cast<const float*>(g.A_scale)[size_t(sa_row) * (K / 128) + k0 / 128]);
   };
@@ -369,27 +376,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
           }
         }
       } else {  // MX
-        // MFMA m: weight lane half h holds the stage's K 128h + 32m .. +32 (window
-        // block h); the fp8 operand lane half h the matching K 32m + 16h .. +16
-        // (chunk 2m + h) and 128 + 32m + 16h .. +16 (chunk 8 + 2m + h); both scales
-        // of lane (row, h) are group 4h + m of the stage.
+        // MFMA m of the stage's KS/64: weight lane half h holds the stage's K
+        // (KS/2)h + 32m .. +32 (window block h); the fp8 operand lane half h the
+        // matching K 32m + 16h .. +16 (chunk 2m + h) and KS/2 + 32m + 16h .. +16
+        // (chunk KS/32 + 2m + h); both scales of lane (row, h) are group
+        // (KS/64)h + m of the stage.
 #pragma unroll
         for (int i = 0; i < MS; ++i) {
           if (i >= act_ms) continue;
           const int ar = i * 32 + l32;
-          const uint2 sa8 = Sa[buf][ar];
-          const uint32_t saw = half ? sa8.y : sa8.x;
+          uint32_t saw;                              // this lane's half of the row's stage scales
+          if constexpr (KS == 256) {
+            const uint2 sa8 = Sa[buf][ar];
+            saw = half ? sa8.y : sa8.x;
+          } else {
+            saw = Sa[buf][ar] >> (16 * half);
+          }
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
+          for (int m = 0; m < KS / 64; ++m) {
             const i32x8 a = rs_cat(*reinterpret_cast<const uint4*>(Ab + rs_swz<AROWB>(ar, 2 * m + half)),
-                                   *reinterpret_cast<const uint4*>(Ab + rs_swz<AROWB>(ar, 8 + 2 * m + half)));
+                                   *reinterpret_cast<const uint4*>(Ab + rs_swz<AROWB>(ar, KS / 32 + 2 * m + half)));
             const int sa = int((saw >> (8 * m)) & 0xffu);
 #pragma unroll
             for (int f = 0; f < 2; ++f) {
               const uint4 bw = breg[buf][f][m];
               const i32x8 b = i32x8{int(bw.x), int(bw.y), int(bw.z), int(bw.w), 0, 0, 0, 0};
               acc[i][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  b, a, acc[i][f], 4, 0, 0, int((sbm[buf][f] >> (8 * m)) & 0xffu), 0, sa);
+                  b, a, acc[i][f], 4, 0, 0, int((uint32_t(sbm[buf][f]) >> (8 * m)) & 0xffu), 0, sa);
             }
           }
         }
