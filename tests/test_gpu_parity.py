@@ -96,11 +96,26 @@ VARIANTS = [
     (C.MINI_FP8, dict(swiglu_limit=0.25)),
     (C.MINI_MXFP4, dict(swiglu_limit=0.25)),
     (C.MINI_MXFP4_WIDE, dict(swiglu_limit=0.25)),
+    (C.MINI_NVFP4, dict(swiglu_limit=0.25)),
     (C.MINI_F32, dict(swiglu_limit=0.2)),
     (C.MINI_GROUPED_BF16, dict(norm_topk_prob=False)),
     (C.MINI_FP8, dict(norm_topk_prob=False)),
     (C.TINY_F32, dict(norm_topk_prob=False, swiglu_limit=0.2)),
 ]
+
+
+def _parity_both_paths(inp):
+    """Stage-wise and fused paths against the oracle; returns the oracle's result."""
+    b = HN.run_stages(inp)
+    ref = HN.oracle(inp)
+    _check_routing(b, ref)
+    _check_permutation(b, ref)
+    tol = HN.TOL[inp.cfg.recipe]
+    err = HN.rel_l2(HN.out_f64(b.out), ref["out"])
+    assert err < tol, f"out rel-L2 {err:.3e}"
+    b2 = HN.run_forward(inp)
+    assert torch.equal(b2.out, b.out)
+    return ref
 
 
 @pytest.mark.parametrize("case", VARIANTS,
@@ -109,18 +124,23 @@ def test_method_variants(case):
     base, kw = case
     cfg = base.replace(**kw)
     inp = G.generate(cfg, device="cuda")             # same tensors as the base workload (same name)
-    b = HN.run_stages(inp)
-    ref = HN.oracle(inp)
-    _check_routing(b, ref)
-    _check_permutation(b, ref)
-    tol = HN.TOL[cfg.recipe]
-    err = HN.rel_l2(HN.out_f64(b.out), ref["out"])
-    assert err < tol, f"out rel-L2 {err:.3e}"
-    b2 = HN.run_forward(inp)
-    assert torch.equal(b2.out, b.out)
+    ref = _parity_both_paths(inp)
     # the variant changes the result well beyond the tolerance
     ref0 = HN.oracle(dataclasses.replace(inp, cfg=base))
-    assert HN.rel_l2(ref["out"], ref0["out"]) > 5 * tol
+    assert HN.rel_l2(ref["out"], ref0["out"]) > 5 * HN.TOL[cfg.recipe]
+
+
+# Smallest fp4 shapes: one 256-deep stage per gate/up tile (and one NVFP4 / two
+# 128-deep MXFP4 down stages), so every register ring runs past its last stage.
+SHAPES = [
+    C.MINI_MXFP4.replace(name="mini_mxfp4_h256", hidden=256, intermediate=256),
+    C.MINI_NVFP4.replace(name="mini_nvfp4_h256", hidden=256, intermediate=256),
+]
+
+
+@pytest.mark.parametrize("cfg", SHAPES, ids=lambda c: c.name)
+def test_smallest_fp4_shapes(cfg):
+    _parity_both_paths(G.generate(cfg, device="cuda"))
 
 
 def _edge_inputs(kind):
