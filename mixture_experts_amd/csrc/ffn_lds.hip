@@ -89,6 +89,18 @@ __device__ __forceinline__ float* lds_f32() {
   return a;
 }
 
+// A third weight slot (instantiated by the PIPE 2 kernels only)
+template <int N>
+__device__ __forceinline__ uint8_t* lds_wslot2() {
+  __shared__ __attribute__((aligned(1024))) uint8_t a[N];
+  return a;
+}
+
+// Workgroup barrier that leaves vector memory loads in flight: __syncthreads()
+// releases every address space and waits for all of them (vmcnt(0)); here each
+// wave has already waited, by count, for the copies the next stage needs.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // One bf16 stage (64 K) for the NJ row fragments of this wave that hold real rows,
 // in 16-deep sub-steps: the operands of sub-step s+1 are read from LDS while the
 // MFMAs of sub-step s run (register double buffer; the order is pinned with
@@ -180,8 +192,10 @@ __device__ __forceinline__ void stage_fp8(f32x4 (&acc)[MU][NC], const uint8_t* A
 
 // MS: 32-row fragments per tile; WM x WN: wavefront grid; PIPE (bf16 only): 1 =
 // the stage barrier sits before the stage's last sub-step, so that stage k+2's
-// copies and stage k+1's first LDS reads overlap stage k's last MFMAs; NB: weight
-// rows per tile (SwiGLU: NB/2 h columns).
+// copies and stage k+1's first LDS reads overlap stage k's last MFMAs; 2 = the
+// same with three weight slots (and two activation slots), so that each
+// stage's weight copies have two stages of compute to land; NB: weight rows per
+// tile (SwiGLU: NB/2 h columns).
 template <int MS, int MODE, int KIND, int WM, int WN, int PIPE = 0, int NB = 256>
 __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
   constexpr int NW = WM * WN;                       // wavefronts
@@ -361,7 +375,109 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
   };
 
   const int KT = K / KS;
-  if constexpr (PIPE == 1 && !FP8) {
+  if constexpr (PIPE == 2 && !FP8) {
+    // ---- bf16 main loop, activation ring of 2 slots, weight ring of 3: stage kt
+    // reads A slot kt % 2 and B slot kt % 3.  At the barrier of stage kt, stage
+    // kt+1 must have landed while stage kt+2's weights (issued last) may still be
+    // in flight; then stage kt+2's activations and stage kt+3's weights refill the
+    // slots stage kt has finished reading.
+    constexpr int NS = ROWB / 32;
+    const int half = lane >> 5, l32 = lane & 31;
+    uint8_t* const Bs2 = lds_wslot2<NB * ROWB>();
+    auto Asl = [&](auto ac) -> uint8_t* { return decltype(ac)::value == 0 ? As0 : As1; };
+    auto Bsl = [&](auto bc) -> uint8_t* {
+      return decltype(bc)::value == 0 ? Bs0 : (decltype(bc)::value == 1 ? Bs1 : Bs2);
+    };
+    auto issue_a = [&](int k0, auto ac) {
+#pragma unroll
+      for (int j = 0; j < A_INSTR; ++j)
+        if ((wave * A_INSTR + j) * (1024 / ROWB) < ti.rows)
+          async_copy16(a_src[j] + size_t(k0) * EB, Asl(ac) + (wave * A_INSTR + j) * 1024);
+    };
+    auto issue_b = [&](int k0, auto bc) {          // B_INSTR copies per wave, always
+      const size_t ko = koff_bytes(k0);
+#pragma unroll
+      for (int j = 0; j < B_INSTR; ++j) async_copy16(b_src[j] + ko, Bsl(bc) + (wave * B_INSTR + j) * 1024);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    auto mainloop = [&](auto njc) {
+      constexpr int NJ = decltype(njc)::value;
+      constexpr int NJA = NJ > 0 ? NJ : 1;
+      bf16x8 bv[2][NF], av[2][NJA];
+      auto rd = [&](auto ac, auto bc, int s, int slot) {
+        if constexpr (NJ > 0) {
+          const int off = l32 * ROWB + (swz_slot(l32, 2 * s + half) << 4);
+          const uint8_t* Aw = Asl(ac) + wm * 32 * ROWB + off;
+          const uint8_t* Bw = Bsl(bc) + brow0 * ROWB + off;
+#pragma unroll
+          for (int f = 0; f < NF; ++f) bv[slot][f] = __builtin_bit_cast(bf16x8, lds16(Bw + bfrag_row<SPLIT, NB>(f) * ROWB));
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) av[slot][j] = __builtin_bit_cast(bf16x8, lds16(Aw + WM * 32 * ROWB * j));
+        }
+      };
+      auto mm = [&](int slot) {
+        if constexpr (NJ > 0) {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int f = 0; f < NF; ++f)
+              acc16[j][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[slot][f], av[slot][j], acc16[j][f], 0, 0, 0);
+        }
+      };
+      auto step = [&](int kt, auto ac, auto bc) {
+        constexpr int a = decltype(ac)::value, b = decltype(bc)::value;
+#pragma unroll
+        for (int s = 0; s < NS - 1; ++s) {
+          rd(ac, bc, s + 1, (s + 1) & 1);
+          sched_fence();
+          mm(s & 1);
+          sched_fence();
+        }
+        if (kt + 1 < KT) {
+          if (kt + 2 < KT) wait_vmcnt<B_INSTR>();   // stage kt+1 has landed (own copies)
+          else wait_vmcnt<0>();
+          lds_barrier();                              // (everyone's); everyone is done reading stage kt
+          if (kt + 2 < KT) issue_a((kt + 2) * KS, ac);
+          if (kt + 3 < KT) issue_b((kt + 3) * KS, bc);
+        }
+        rd(std::integral_constant<int, a ^ 1>{}, std::integral_constant<int, (b + 1) % 3>{}, 0, 0);
+        sched_fence();
+        mm((NS - 1) & 1);
+        sched_fence();
+      };
+      rd(I0{}, I0{}, 0, 0);
+      int kt = 0;
+      for (; kt + 5 < KT; kt += 6) {
+        step(kt, I0{}, I0{});
+        step(kt + 1, I1{}, I1{});
+        step(kt + 2, I0{}, I2{});
+        step(kt + 3, I1{}, I0{});
+        step(kt + 4, I0{}, I1{});
+        step(kt + 5, I1{}, I2{});
+      }
+      if (kt < KT) step(kt, I0{}, I0{});
+      if (kt + 1 < KT) step(kt + 1, I1{}, I1{});
+      if (kt + 2 < KT) step(kt + 2, I0{}, I2{});
+      if (kt + 3 < KT) step(kt + 3, I1{}, I0{});
+      if (kt + 4 < KT) step(kt + 4, I0{}, I1{});
+    };
+    issue_a(0, I0{});
+    issue_b(0, I0{});
+    if (KT > 1) {
+      issue_a(KS, I1{});
+      issue_b(KS, I1{});
+    }
+    if (KT > 2) issue_b(2 * KS, I2{});
+    wait_vmcnt<0>();                                // (a wave's copy count varies with the tile's rows)
+    __syncthreads();
+    if (MW >= 4 && nj == 4) mainloop(std::integral_constant<int, (MW >= 4 ? 4 : 0)>{});
+    else if (MW >= 3 && nj == 3) mainloop(std::integral_constant<int, (MW >= 3 ? 3 : 0)>{});
+    else if (MW >= 2 && nj == 2) mainloop(std::integral_constant<int, (MW >= 2 ? 2 : 0)>{});
+    else if (nj == 1) mainloop(std::integral_constant<int, 1>{});
+    else mainloop(std::integral_constant<int, 0>{});
+  } else if constexpr (PIPE == 1 && !FP8) {
     // ---- bf16 main loop, barrier before the last sub-step.  Every wave runs it,
     // also one without real rows (its copies and barriers are shared).
     constexpr int NS = ROWB / 32;
@@ -575,15 +691,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
 
 template <int MS, int MODE, int KIND, int WM, int WN, int PIPE = 0, int NB = 256>
 void launch_lds_variant(const GemmArgs& g, int m_tiles, hipStream_t st) {
-  constexpr size_t lds = size_t(NST) * (MS * 32 + NB) * ROWB + (KIND == KIND_FP8 ? size_t(NST + WN) * MS * 32 * 4 + 32 : 0);
+  constexpr size_t lds = size_t(NST) * (MS * 32 + NB) * ROWB + (PIPE == 2 ? size_t(NB) * ROWB : 0) +
+                         (KIND == KIND_FP8 ? size_t(NST + WN) * MS * 32 * 4 + 32 : 0);
   static_assert(lds <= 160 * 1024, "LDS budget");
   const int ncols = (MODE == EPI_SWIGLU) ? g.N / (NB / 2) : (g.N + NB - 1) / NB;
   ffn_lds_kernel<MS, MODE, KIND, WM, WN, PIPE, NB><<<dim3(ncols, m_tiles), 64 * WM * WN, 0, st>>>(g);
 }
 
 // Production configurations.  bf16: 256-row tiles on 2 x 4 wavefronts (two per
-// SIMD) with the stage barrier before the last sub-step; smaller tiles on 2 x 2
-// wavefronts.  fp8: 2 x 4 wavefronts, 256-row tiles: the block-scale FMAs keep
+// SIMD) with the stage barrier before the last sub-step and a three-slot weight
+// ring (all 160 KB of LDS); smaller tiles on 2 x 2 wavefronts.  fp8: 2 x 4 wavefronts, 256-row tiles: the block-scale FMAs keep
 // the accumulators in ordinary VGPRs, and a second wave per SIMD overlaps one
 // wave's FMAs with the other's MFMAs.
 template <int MODE, int KIND>
@@ -594,7 +711,7 @@ static hipError_t launch_lds_ms(int ms, int m_tiles, const GemmArgs& g, hipStrea
   } else {
     if (ms <= 2) launch_lds_variant<2, MODE, KIND, 2, 2>(g, m_tiles, st);
     else if (ms <= 4) launch_lds_variant<4, MODE, KIND, 2, 2>(g, m_tiles, st);
-    else launch_lds_variant<8, MODE, KIND, 2, 4, 1>(g, m_tiles, st);
+    else launch_lds_variant<8, MODE, KIND, 2, 4, 2>(g, m_tiles, st);
   }
   return hipGetLastError();
 }
