@@ -32,6 +32,8 @@
 // activation block meet in that XCD's L2.  The row tiles of one expert read the
 // same weight rows, but far apart in time, so each of them streams the weights
 // from HBM again; experts of 257..511 rows therefore pay two weight passes.
+#include <cstdlib>
+
 #include "gemm_common.h"
 #include "kernels.h"
 
@@ -46,6 +48,16 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Slot of logical 16-byte chunk c in LDS row r.
 __device__ __forceinline__ int swz_slot(int r, int c) { return c ^ ((r ^ (r >> 1)) & 7); }
+
+// Async global -> LDS copy through a buffer descriptor (MUBUF): unlike the FLAT
+// form, an outstanding copy of this kind does not stop the compiler from
+// counting LDS reads (lgkmcnt) precisely.
+__device__ __forceinline__ void buf_copy16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds_wave_base, 16, int(voff), int(soff), 0, 0);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), short(0), -1, 0x00020000);
+}
 
 __device__ __forceinline__ void async_copy16(const void* g, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_wave_base, 16, 0, 0);
@@ -196,7 +208,7 @@ __device__ __forceinline__ void stage_fp8(f32x4 (&acc)[MU][NC], const uint8_t* A
 // same with three weight slots (and two activation slots), so that each
 // stage's weight copies have two stages of compute to land; NB: weight rows per
 // tile (SwiGLU: NB/2 h columns).
-template <int MS, int MODE, int KIND, int WM, int WN, int PIPE = 0, int NB = 256>
+template <int MS, int MODE, int KIND, int WM, int WN, int PIPE, int NB, bool BUF>
 __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
   constexpr int NW = WM * WN;                       // wavefronts
   constexpr int BM = MS * 32;
@@ -249,12 +261,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
   // ---- global sources of this thread's async copies: copy j of wave w fills LDS
   // chunk positions p = (w*INSTR + j)*64 + lane -> row p / 8, slot p % 8, logical
   // chunk slot ^ key(row)
-  const uint8_t* a_src[A_INSTR];
+  // (BUF: byte offsets below 2^32 from A and from the tile's expert weights, copied
+  // through buffer descriptors; else 64-bit addresses, copied with the FLAT form)
+  using Src = std::conditional_t<BUF, uint32_t, const uint8_t*>;
+  Src a_src[A_INSTR];
 #pragma unroll
   for (int j = 0; j < A_INSTR; ++j) {
     const int p = (wave * A_INSTR + j) * 64 + lane, r = p / (ROWB / 16);
     const int c = swz_slot(r, p % (ROWB / 16));
-    a_src[j] = A + size_t(a_row(g, ti.row0 + min(r, ti.rows - 1))) * g.lda * EB + c * 16;
+    const size_t off = size_t(a_row(g, ti.row0 + min(r, ti.rows - 1))) * g.lda * EB + c * 16;
+    if constexpr (BUF) a_src[j] = uint32_t(off);
+    else a_src[j] = A + off;
   }
   int n0, sub0 = 0;
   if (MODE == EPI_SWIGLU) {
@@ -263,7 +280,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
   } else {
     n0 = nt * NB;
   }
-  const uint8_t* b_src[B_INSTR];
+  const uint8_t* const B0 = B + (MODE == EPI_SWIGLU ? size_t(sub0) * 2 * ns * size_t(K)
+                                                    : size_t(ti.e) * g.n_experts_split * g.N * ns) * EB;
+  Src b_src[B_INSTR];
 #pragma unroll
   for (int j = 0; j < B_INSTR; ++j) {
     const int p = (wave * B_INSTR + j) * 64 + lane, r = p / (ROWB / 16);
@@ -271,13 +290,22 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
     size_t rowoff;
     if (MODE == EPI_SWIGLU) {
       const int wr = (r < NB / 2) ? (n0 % ns + r) : (ns + n0 % ns + r - NB / 2);
-      rowoff = (size_t(sub0) * 2 * ns + wr) * size_t(K);
+      rowoff = size_t(wr) * size_t(K);
     } else {
       const int n = min(n0 + r, g.N - 1);
-      rowoff = size_t(ti.e) * g.n_experts_split * g.N * ns + size_t(n) * ns;
+      rowoff = size_t(n) * ns;
     }
-    b_src[j] = B + rowoff * EB + c * 16;
+    if constexpr (BUF) b_src[j] = uint32_t(rowoff * EB + c * 16);
+    else b_src[j] = B0 + rowoff * EB + c * 16;
   }
+  auto copy_a = [&](int j, int k0, void* lds) {
+    if constexpr (BUF) buf_copy16(buf_rsrc(A), a_src[j], uint32_t(k0 * EB), lds);
+    else async_copy16(a_src[j] + size_t(k0) * EB, lds);
+  };
+  auto copy_b = [&](int j, size_t ko, void* lds) {
+    if constexpr (BUF) buf_copy16(buf_rsrc(B0), b_src[j], uint32_t(ko), lds);
+    else async_copy16(b_src[j] + ko, lds);
+  };
   auto koff_bytes = [&](int k0) -> size_t {
     if (MODE == EPI_SWIGLU) return size_t(k0) * EB;
     return (size_t(k0 / ns) * g.N * ns + (k0 % ns)) * EB;
@@ -301,10 +329,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < A_INSTR; ++j)
       if ((wave * A_INSTR + j) * (1024 / ROWB) < ti.rows)
-        async_copy16(a_src[j] + size_t(k0) * EB, As(buf) + (wave * A_INSTR + j) * 1024);
+        copy_a(j, k0, As(buf) + (wave * A_INSTR + j) * 1024);
     const size_t ko = koff_bytes(k0);
 #pragma unroll
-    for (int j = 0; j < B_INSTR; ++j) async_copy16(b_src[j] + ko, Bs(buf) + (wave * B_INSTR + j) * 1024);
+    for (int j = 0; j < B_INSTR; ++j) copy_b(j, ko, Bs(buf) + (wave * B_INSTR + j) * 1024);
     if (FP8) {
       const float* SA = static_cast<const float*>(g.A_scale);
       sa_reg[buf] = SA[size_t(sa_row) * (K / 128) + k0 / 128];
@@ -392,12 +420,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < A_INSTR; ++j)
         if ((wave * A_INSTR + j) * (1024 / ROWB) < ti.rows)
-          async_copy16(a_src[j] + size_t(k0) * EB, Asl(ac) + (wave * A_INSTR + j) * 1024);
+          copy_a(j, k0, Asl(ac) + (wave * A_INSTR + j) * 1024);
     };
     auto issue_b = [&](int k0, auto bc) {          // B_INSTR copies per wave, always
       const size_t ko = koff_bytes(k0);
 #pragma unroll
-      for (int j = 0; j < B_INSTR; ++j) async_copy16(b_src[j] + ko, Bsl(bc) + (wave * B_INSTR + j) * 1024);
+      for (int j = 0; j < B_INSTR; ++j) copy_b(j, ko, Bsl(bc) + (wave * B_INSTR + j) * 1024);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -689,13 +717,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
   }
 }
 
-template <int MS, int MODE, int KIND, int WM, int WN, int PIPE = 0, int NB = 256>
+template <int MS, int MODE, int KIND, bool BUF, int WM, int WN, int PIPE = 0, int NB = 256>
 void launch_lds_variant(const GemmArgs& g, int m_tiles, hipStream_t st) {
   constexpr size_t lds = size_t(NST) * (MS * 32 + NB) * ROWB + (PIPE == 2 ? size_t(NB) * ROWB : 0) +
                          (KIND == KIND_FP8 ? size_t(NST + WN) * MS * 32 * 4 + 32 : 0);
   static_assert(lds <= 160 * 1024, "LDS budget");
   const int ncols = (MODE == EPI_SWIGLU) ? g.N / (NB / 2) : (g.N + NB - 1) / NB;
-  ffn_lds_kernel<MS, MODE, KIND, WM, WN, PIPE, NB><<<dim3(ncols, m_tiles), 64 * WM * WN, 0, st>>>(g);
+  ffn_lds_kernel<MS, MODE, KIND, WM, WN, PIPE, NB, BUF><<<dim3(ncols, m_tiles), 64 * WM * WN, 0, st>>>(g);
 }
 
 // Production configurations.  bf16: 256-row tiles on 2 x 4 wavefronts (two per
@@ -703,26 +731,40 @@ void launch_lds_variant(const GemmArgs& g, int m_tiles, hipStream_t st) {
 // ring (all 160 KB of LDS); smaller tiles on 2 x 2 wavefronts.  fp8: 2 x 4 wavefronts, 256-row tiles: the block-scale FMAs keep
 // the accumulators in ordinary VGPRs, and a second wave per SIMD overlaps one
 // wave's FMAs with the other's MFMAs.
-template <int MODE, int KIND>
+template <int MODE, int KIND, bool BUF>
 static hipError_t launch_lds_ms(int ms, int m_tiles, const GemmArgs& g, hipStream_t st) {
   if constexpr (KIND == KIND_FP8) {
-    if (ms <= 4) launch_lds_variant<4, MODE, KIND, 2, 4>(g, m_tiles, st);
-    else launch_lds_variant<8, MODE, KIND, 2, 4>(g, m_tiles, st);
+    if (ms <= 4) launch_lds_variant<4, MODE, KIND, BUF, 2, 4>(g, m_tiles, st);
+    else launch_lds_variant<8, MODE, KIND, BUF, 2, 4>(g, m_tiles, st);
   } else {
-    if (ms <= 2) launch_lds_variant<2, MODE, KIND, 2, 2>(g, m_tiles, st);
-    else if (ms <= 4) launch_lds_variant<4, MODE, KIND, 2, 2>(g, m_tiles, st);
-    else launch_lds_variant<8, MODE, KIND, 2, 4, 2>(g, m_tiles, st);
+    if (ms <= 2) launch_lds_variant<2, MODE, KIND, BUF, 2, 2>(g, m_tiles, st);
+    else if (ms <= 4) launch_lds_variant<4, MODE, KIND, BUF, 2, 2>(g, m_tiles, st);
+    else launch_lds_variant<8, MODE, KIND, BUF, 2, 4, 2>(g, m_tiles, st);
   }
   return hipGetLastError();
 }
 
+// Buffer-descriptor copies address A and the tile's expert weights with 32-bit
+// offsets: usable when a_rows is known and both extents stay below 4 GiB.  The
+// environment variable MOE_LDS_FLAT forces the FLAT-copy form (to test it).
+template <int MODE, int KIND>
+static hipError_t launch_lds_any(int ms, int m_tiles, const GemmArgs& g, hipStream_t st) {
+  constexpr int64_t eb = KIND == KIND_FP8 ? 1 : 2, lim = (int64_t(1) << 32) - 256;
+  const int64_t a_bytes = g.a_rows * g.lda * eb;
+  const int64_t b_bytes = MODE == EPI_SWIGLU ? 2 * int64_t(g.nsplit) * g.K * eb
+                                             : int64_t(g.n_experts_split) * g.N * g.nsplit * eb;
+  if (g.a_rows > 0 && a_bytes < lim && b_bytes < lim && std::getenv("MOE_LDS_FLAT") == nullptr)
+    return launch_lds_ms<MODE, KIND, true>(ms, m_tiles, g, st);
+  return launch_lds_ms<MODE, KIND, false>(ms, m_tiles, g, st);
+}
+
 hipError_t launch_lds_swiglu(bool fp8, int ms, int m_tiles, const GemmArgs& g, hipStream_t st) {
-  return fp8 ? launch_lds_ms<EPI_SWIGLU, KIND_FP8>(ms, m_tiles, g, st)
-             : launch_lds_ms<EPI_SWIGLU, KIND_BF16>(ms, m_tiles, g, st);
+  return fp8 ? launch_lds_any<EPI_SWIGLU, KIND_FP8>(ms, m_tiles, g, st)
+             : launch_lds_any<EPI_SWIGLU, KIND_BF16>(ms, m_tiles, g, st);
 }
 hipError_t launch_lds_down(bool fp8, int ms, int m_tiles, const GemmArgs& g, hipStream_t st) {
-  return fp8 ? launch_lds_ms<EPI_STORE, KIND_FP8>(ms, m_tiles, g, st)
-             : launch_lds_ms<EPI_STORE, KIND_BF16>(ms, m_tiles, g, st);
+  return fp8 ? launch_lds_any<EPI_STORE, KIND_FP8>(ms, m_tiles, g, st)
+             : launch_lds_any<EPI_STORE, KIND_BF16>(ms, m_tiles, g, st);
 }
 
 }  // namespace moe

@@ -12,6 +12,8 @@ enum EpiMode { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_COMBINE = 2 };
 //   where tiles = {count, e_0, m0_0, e_1, m0_1, ...}.  Dense mode: one expert, rows 0..dense_rows.
 struct GemmArgs {
   const void* A;            // activations [rows][K] (bf16, fp32 or fp8 codes)
+  int64_t a_rows;           // rows of A a launch may address (0: unknown); lets the
+                            // LDS-staged kernel use 32-bit buffer offsets when small
   const void* A_scale;      // activation scales (fp8: fp32 [rows][K/128]; MX: E8M0 [rows][K/32])
   int lda;
   const int32_t* offsets;   // [E+1]

@@ -210,6 +210,7 @@ hipError_t launch_grouped_ffn(const moe_config_t& c, const int32_t* offsets, con
   g.A_scale = x_perm_scale;
   g.a_map = a_map;
   g.a_div = c.top_k;
+  g.a_rows = a_map ? int64_t(c.num_tokens) : int64_t(c.num_tokens) * c.top_k;
   g.lda = c.hidden;
   g.offsets = offsets;
   g.B = w.w13;
@@ -242,6 +243,7 @@ hipError_t launch_grouped_ffn(const moe_config_t& c, const int32_t* offsets, con
   d.A = s.h;
   d.A_scale = s.h_scale;
   d.a_map = nullptr;                                   // h rows are in pair order
+  d.a_rows = int64_t(c.num_tokens) * c.top_k;
   d.lda = c.intermediate;
   d.B = w.w2;
   d.B_scale = w.w2_scale;
@@ -326,6 +328,7 @@ hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32
   GemmArgs g{};
   g.swiglu_limit = c.swiglu_limit;
   g.A = x;
+  g.a_rows = T;
   g.lda = c.hidden;
   g.dense_rows = T;
   g.B = shared->w13;
