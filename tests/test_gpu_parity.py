@@ -143,10 +143,12 @@ def test_smallest_fp4_shapes(cfg):
     _parity_both_paths(G.generate(cfg, device="cuda"))
 
 
-# The LDS-staged kernels copy through buffer descriptors (32-bit offsets) when A
-# and the expert weights fit 4 GiB, else with 64-bit FLAT copies; MOE_LDS_FLAT
-# forces the second form, which no test shape would reach otherwise.
-@pytest.mark.parametrize("cfg", [C.MINI_PREFILL_BF16, C.MINI_PREFILL_FP8, C.MINI_MIXED_BF16], ids=lambda c: c.name)
+# The LDS-staged kernels (and the register-streaming kernel for MXFP4 / NVFP4)
+# copy through buffer descriptors (32-bit offsets) when A and the expert weights
+# fit 4 GiB, else with 64-bit FLAT copies; MOE_LDS_FLAT forces the second form,
+# which no test shape would reach otherwise.
+@pytest.mark.parametrize("cfg", [C.MINI_PREFILL_BF16, C.MINI_PREFILL_FP8, C.MINI_MIXED_BF16, C.MINI_MXFP4_WIDE,
+                                 C.MINI_NVFP4], ids=lambda c: c.name)
 def test_lds_flat_copy_form(cfg, monkeypatch):
     monkeypatch.setenv("MOE_LDS_FLAT", "1")
     _parity_both_paths(G.generate(cfg, device="cuda"))
