@@ -5,6 +5,8 @@
 // 3.2 + e_score_correction_bias, group top-2 sums, keep topk_group groups, top-k;
 // 3.3 normalise the k picked scores to sum 1, times routed_scaling_factor.
 // sqrtsoftplus is the DeepSeek-V4-Pro score (lzwjava.github.io, architecture).
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace moe {
@@ -281,20 +283,23 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ l
 
 // ---------------------------------------------------------------------------
 // K splits of the gate GEMM: the d (a divisor of the K chunks, <= 32) with the
-// least estimated time.  Two 128 x 64 blocks fit a CU (LDS), so a launch runs in
-// ceil(blocks / 512) rounds of K/d chunks each; every split beyond the first adds
-// a T x E fp64 partial written once and read once.  Per-chunk time and bandwidth
-// are round figures for the fp64 MFMA rate and HBM.
+// least estimated time.  The kernel is fp64-MFMA bound and two 128 x 64 blocks
+// share a CU (LDS), so a CU that holds L blocks takes L times as long as one
+// block alone would with a second one beside it, and a lone block leaves half its
+// CU's issue slots unused: time ~ (max(L, 2) + 1/2) * (K/d chunks), L =
+// ceil(blocks / 256), the half block for the uneven finish of the last ones.
+// Every split beyond the first adds a T x E fp64 partial written once and read
+// once.  Per-chunk time and bandwidth are round measured figures.
 int gate_ksplit(const moe_config_t& c) {
   const int tiles = ((c.num_experts + GE - 1) / GE) * ((c.num_tokens + GT - 1) / GT);
   const int steps = c.hidden / GK;
-  constexpr double chunk_s = 3.4e-6, bytes_per_s = 5e12;
+  constexpr double chunk_s = 1.7e-6, bytes_per_s = 5e12;
   int best = 1;
   double best_t = 0.0;
   for (int d = 1; d <= steps && d <= 32; ++d) {
     if (steps % d) continue;
-    const double rounds = double((int64_t(tiles) * d + 511) / 512);
-    const double t = rounds * (steps / d) * chunk_s +
+    const int64_t per_cu = (int64_t(tiles) * d + 255) / 256;
+    const double t = (double(std::max<int64_t>(per_cu, 2)) + 0.5) * (steps / d) * chunk_s +
                      (d > 1 ? double(d) * c.num_tokens * c.num_experts * 16.0 / bytes_per_s : 0.0);
     if (d == 1 || t < 0.97 * best_t) {             // a split must win clearly
       best = d;
