@@ -590,6 +590,12 @@ static void rs_launch_t(int ms, dim3 grid, const GemmArgs& g, hipStream_t st) {
       return;
     }
   }
+  if constexpr (RECIPE == MOE_RECIPE_FP8_B128) {
+    if (ms == 3) {                                 // 96-row tiles (fp8's 128-row tile spills), two waves per SIMD
+      ffn_rs_kernel<3, MODE, RECIPE, 2, 2, BUF><<<grid, 256, 0, st>>>(g);
+      return;
+    }
+  }
   // NVFP4's stages carry fp16 activations four times as deep as bf16's: one more stage in flight
   if (ms <= 1)
     ffn_rs_kernel<1, MODE, RECIPE, (RECIPE == MOE_RECIPE_NVFP4 ? 3 : RS_NST1), 1, BUF><<<grid, 256, 0, st>>>(g);
@@ -622,7 +628,7 @@ static hipError_t rs_launch_recipe(int recipe, int ms, dim3 grid, const GemmArgs
   return hipGetLastError();
 }
 
-// Tiles of ms*32 rows (ms = 1 or 2; bf16, MXFP4 and NVFP4 also 4).  bf16 is used for the shared experts of every
+// Tiles of ms*32 rows (ms = 1 or 2; bf16, MXFP4 and NVFP4 also 4, fp8 also 3).  bf16 is used for the shared experts of every
 // bf16-activation recipe as well.
 hipError_t launch_rs_swiglu(int recipe, int ms, int m_tiles, const GemmArgs& g, hipStream_t st) {
   return rs_launch_recipe<EPI_SWIGLU>(recipe, ms, dim3(g.N / 128, m_tiles), g, st);
