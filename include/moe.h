@@ -38,6 +38,10 @@
  *     MOE_ERR_WORKSPACE_TOO_SMALL.  MOE_ERR_LAUNCH reports a failed kernel
  *     launch.  Faults inside kernels surface at the caller's next
  *     synchronisation.  num_tokens == 0 returns MOE_OK and enqueues nothing.
+ *   - Environment: MOE_LDS_FLAT (any value) makes the GEMM kernels copy
+ *     activations and weights into LDS with 64-bit addresses even where the
+ *     tensors fit 32-bit buffer offsets (the faster form).  Results are the
+ *     same either way; the switch exists to test the 64-bit form.
  *   - Matrices are row-major.  Weights use the [out, in] convention of the
  *     checkpoints (the gate matrix is [E, H], 384 x 7168 in the walk-through).
  *
