@@ -11,9 +11,13 @@
 // row fragments in every wave and costs MFMA time in proportion to its rows.
 //
 // Both operands are staged through LDS with gfx950's direct global->LDS 16-byte
-// loads (global_load_lds_dwordx4) into a two-slot ring of 128-byte rows (64 bf16
-// or 128 fp8 of K per stage; whole cache lines per row): one stage is in flight
-// while the other is consumed.  The 16-byte chunk c of LDS row r sits at slot
+// loads into rings of 128-byte rows (64 bf16 or 128 fp8 of K per stage; whole
+// cache lines per row): two slots per operand, and for the 256-row bf16 tiles a
+// third weight slot, so that the weight copies run two stages ahead.  The copies
+// use the buffer-descriptor form (buffer_load_dwordx4 ... lds, 32-bit offsets)
+// when the tensors allow it: while a FLAT-form copy (global_load_lds_dwordx4) is
+// outstanding, the compiler cannot order the LDS fragment reads against it and
+// waits for all of them before every MFMA group.  The 16-byte chunk c of LDS row r sits at slot
 // c ^ ((r ^ (r>>1)) & 7): any 16 consecutive rows reading one chunk hit 16
 // distinct 16-byte slots of a 256-byte bank window.  The XOR is applied on the
 // global side, so the LDS writes of one copy instruction (64 lanes x 16 bytes)
