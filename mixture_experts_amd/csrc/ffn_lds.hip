@@ -17,7 +17,9 @@
 // use the buffer-descriptor form (buffer_load_dwordx4 ... lds, 32-bit offsets)
 // when the tensors allow it: while a FLAT-form copy (global_load_lds_dwordx4) is
 // outstanding, the compiler cannot order the LDS fragment reads against it and
-// waits for all of them before every MFMA group.  The 16-byte chunk c of LDS row r sits at slot
+// waits for all of them before every MFMA group.
+//
+// The 16-byte chunk c of LDS row r sits at slot
 // c ^ ((r ^ (r>>1)) & 7): any 16 consecutive rows reading one chunk hit 16
 // distinct 16-byte slots of a 256-byte bank window.  The XOR is applied on the
 // global side, so the LDS writes of one copy instruction (64 lanes x 16 bytes)
