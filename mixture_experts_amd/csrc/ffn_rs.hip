@@ -422,6 +422,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
       }
     }
   }
+  // The surplus stages issued past the end (EVERY) may still be copying into LDS:
+  // a workgroup must not end with copies into LDS that a later one may own.
+  if constexpr (EVERY) rs_wait_vmcnt<0>();
 
   // ---- epilogues.  bf16: lane l, register r of row block i holds token row
   // i*32 + acc_row(r, l) and column l & 31 of the fragment (measured faster for
