@@ -130,16 +130,23 @@ def test_method_variants(case):
     assert HN.rel_l2(ref["out"], ref0["out"]) > 5 * HN.TOL[cfg.recipe]
 
 
-# Smallest fp4 shapes: one 256-deep stage per gate/up tile (and one NVFP4 / two
-# 128-deep MXFP4 down stages), so every register ring runs past its last stage.
 SHAPES = [
+    # smallest fp4 shapes: one 256-deep stage per gate/up tile (and one NVFP4 / two
+    # 128-deep MXFP4 down stages), so every register ring runs past its last stage
     C.MINI_MXFP4.replace(name="mini_mxfp4_h256", hidden=256, intermediate=256),
     C.MINI_NVFP4.replace(name="mini_nvfp4_h256", hidden=256, intermediate=256),
+    # token counts whose average rows per expert select the register-streaming
+    # tile heights no other workload reaches: bf16 64 rows (40 < avg <= 48), fp8
+    # 32 and 64 rows, MXFP4 32 rows (avg <= 24)
+    C.MINI_GROUPED_BF16.replace(name="mini_grouped_bf16_t240", num_tokens=240),
+    C.MINI_FP8.replace(name="mini_fp8_t40", num_tokens=40),
+    C.MINI_FP8.replace(name="mini_fp8_t180", num_tokens=180),
+    C.MINI_MXFP4.replace(name="mini_mxfp4_t64", num_tokens=64),
 ]
 
 
 @pytest.mark.parametrize("cfg", SHAPES, ids=lambda c: c.name)
-def test_smallest_fp4_shapes(cfg):
+def test_more_shapes(cfg):
     _parity_both_paths(G.generate(cfg, device="cuda"))
 
 
