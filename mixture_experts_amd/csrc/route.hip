@@ -6,6 +6,7 @@
 // 3.3 normalise the k picked scores to sum 1, times routed_scaling_factor.
 // sqrtsoftplus is the DeepSeek-V4-Pro score (lzwjava.github.io, architecture).
 #include <algorithm>
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -21,8 +22,8 @@ namespace moe {
 // fp64 MFMA 16x16x4: a 128 x 64 (token x expert) tile per 256-thread block; wave w
 // owns tokens 32w .. 32w+31 against all 64 experts (2 x 4 MFMA tiles).  K runs in
 // chunks of 32, staged through LDS as fp32 (bf16 widens exactly) in a two-slot
-// ring: the next chunk's global loads (16 bytes per lane) are in flight while the
-// current chunk is multiplied.  Within a chunk, lane group g = lane / 16 takes
+// ring; the global loads (16 bytes per lane) of the next two chunks are in flight
+// in two register sets while the current chunk is multiplied.  Within a chunk, lane group g = lane / 16 takes
 // k = 8g .. 8g+7 over the chunk's 8 MFMA steps (the same K order for both
 // operands), so that each lane reads its 8 k of a row with two 16-byte LDS reads.
 // ---------------------------------------------------------------------------
@@ -57,9 +58,11 @@ __global__ __launch_bounds__(256) void gate_logits_f64(const XT* __restrict__ x,
 
   // global -> register loads of one chunk (rows past T / E read row 0 and store 0)
   using LA = GateLoad<XT>;
-  LA la;
-  float4 lb[2];                                     // Wg: 64 rows x 8 segments of 4 floats
-  auto load = [&](int k0) {
+  LA las[2];                                        // two register sets: chunks c and c+1 in flight
+  float4 lbs[2][2];                                 // Wg: 64 rows x 8 segments of 4 floats
+  auto load = [&](int k0, auto setc) {
+    LA& la = las[decltype(setc)::value];
+    float4 (&lb)[2] = lbs[decltype(setc)::value];
 #pragma unroll
     for (int i = 0; i < LA::N; ++i) {
       const int idx = tid + 256 * i, row = idx / LA::PER_ROW, seg = idx % LA::PER_ROW;
@@ -74,7 +77,9 @@ __global__ __launch_bounds__(256) void gate_logits_f64(const XT* __restrict__ x,
       lb[i] = *reinterpret_cast<const float4*>(wg + size_t(e) * H + k0 + seg * 4);
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](auto setc, int buf) {
+    const LA& la = las[decltype(setc)::value];
+    const float4 (&lb)[2] = lbs[decltype(setc)::value];
 #pragma unroll
     for (int i = 0; i < LA::N; ++i) {
       const int idx = tid + 256 * i, row = idx / LA::PER_ROW, seg = idx % LA::PER_ROW;
@@ -107,23 +112,26 @@ __global__ __launch_bounds__(256) void gate_logits_f64(const XT* __restrict__ x,
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
 
-  load(kbeg);
-  store(0);
-  __syncthreads();
-  for (int c = 0; c < nch; ++c) {
-    const int buf = c & 1;
-    if (c + 1 < nch) load(kbeg + (c + 1) * GK);     // in flight during this chunk's MFMAs
+  // Chunk c is multiplied from LDS slot c & 1 while chunks c+1 and c+2 are in
+  // flight into register set (c+1) & 1 and c & 1; chunk c+1 goes to the other LDS
+  // slot after the MFMAs.  The barrier leaves the register loads in flight (a
+  // fenced __syncthreads would wait for them).
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  auto chunk = [&](int c, auto setc) {
+    constexpr int st = decltype(setc)::value;
+    if (c + 2 < nch) load(kbeg + (c + 2) * GK, setc);   // set st held chunk c, already in LDS
     float a[2][8], b[4][8];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const float* p = &As[buf][wave * 32 + 16 * i + r16][8 * g];
+      const float* p = &As[st][wave * 32 + 16 * i + r16][8 * g];
       const float4 lo = *reinterpret_cast<const float4*>(p), hi = *reinterpret_cast<const float4*>(p + 4);
       a[i][0] = lo.x; a[i][1] = lo.y; a[i][2] = lo.z; a[i][3] = lo.w;
       a[i][4] = hi.x; a[i][5] = hi.y; a[i][6] = hi.z; a[i][7] = hi.w;
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float* p = &Bs[buf][16 * j + r16][8 * g];
+      const float* p = &Bs[st][16 * j + r16][8 * g];
       const float4 lo = *reinterpret_cast<const float4*>(p), hi = *reinterpret_cast<const float4*>(p + 4);
       b[j][0] = lo.x; b[j][1] = lo.y; b[j][2] = lo.z; b[j][3] = lo.w;
       b[j][4] = hi.x; b[j][5] = hi.y; b[j][6] = hi.z; b[j][7] = hi.w;
@@ -135,9 +143,19 @@ __global__ __launch_bounds__(256) void gate_logits_f64(const XT* __restrict__ x,
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(a[i][q]), double(b[j][q]), acc[i][j], 0, 0, 0);
-    if (c + 1 < nch) store(buf ^ 1);                 // the slot read in the previous chunk
-    __syncthreads();
+    if (c + 1 < nch) store(std::integral_constant<int, st ^ 1>{}, st ^ 1);   // the slot read in the previous chunk
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  load(kbeg, S0{});
+  if (nch > 1) load(kbeg + GK, S1{});
+  store(S0{}, 0);
+  __syncthreads();
+  int c = 0;
+  for (; c + 1 < nch; c += 2) {
+    chunk(c, S0{});
+    chunk(c + 1, S1{});
   }
+  if (c < nch) chunk(c, S0{});
   // D[i][j]: lane holds column j = lane % 16, rows 4 * r + lane / 16
 #pragma unroll
   for (int i = 0; i < 2; ++i)
