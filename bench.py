@@ -136,7 +136,7 @@ def main():
     inp = G.generate(cfg, device="cuda")
     mcfg = M.make_config(cfg)
     b = M.alloc_buffers(mcfg, "cuda")
-    ex = M.make_weights(inp.w13, inp.w2, inp.w13_scale, inp.w2_scale)
+    ex = M.make_expert_weights(cfg.recipe, inp.w13, inp.w2, inp.w13_scale, inp.w2_scale)   # fp4: scales packed once
     sh = M.make_weights(inp.shared_w13, inp.shared_w2) if cfg.num_shared > 0 else None
     torch.cuda.synchronize()
     print(f"[bench] {cfg.name}: inputs ready in {time.time() - t_gen:.1f} s", file=sys.stderr, flush=True)

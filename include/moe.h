@@ -19,7 +19,10 @@
  *   moe_forward      - all of the above in one call;
  *   moe_rmsnorm, moe_forward_residual - the decoder layer around the MoE
  *                      (section 3.5): post_attention_layernorm in front, the
- *                      residual added in the combine.
+ *                      residual added in the combine;
+ *   moe_pack_fp4_scales - weight preparation (once per set of weights, outside
+ *                      the layer call): MXFP4 / NVFP4 weight scales into the
+ *                      packed layout the routed-expert GEMMs read.
  *
  * Conventions for every entry point
  *   - Every buffer pointer is a DEVICE pointer owned by the caller; the library
@@ -140,8 +143,10 @@ typedef struct {
  *        (MXFP4, NVFP4: [n][2*I][H/2] bytes);
  *   w2:  [n][H][I]    down_proj (MXFP4, NVFP4: [n][H][I/2] bytes);
  *   w13_scale, w2_scale: FP8_B128: fp32 [n][2I/128][H/128] and [n][H/128][I/128];
- *                        MXFP4: E8M0 bytes [n][2I][H/32] and [n][H][I/32];
- *                        NVFP4: e4m3fn codes [n][2I][H/16] and [n][H][I/16];
+ *                        MXFP4: E8M0 bytes, NVFP4: e4m3fn codes, one per G = 32
+ *                        (MXFP4) or 16 (NVFP4) input channels, in the PACKED
+ *                        layout that moe_pack_fp4_scales writes from the
+ *                        row-major [n*2I][H/G] and [n*H][I/G] arrays;
  *                        other recipes: unused (may be NULL).
  * n = num_experts for routed experts; n = num_shared for the shared experts,
  * whose I is shared_intermediate and which always use the plain (F32 or BF16)
@@ -232,6 +237,29 @@ moe_status_t moe_forward_residual(const moe_config_t* cfg, const void* resid, co
                                   const moe_weights_t* experts, const moe_weights_t* shared,
                                   void* out, int32_t* topk_idx_out, float* topk_w_out, void* ws,
                                   size_t ws_bytes, void* stream);
+
+/* Weight preparation for the MXFP4 and NVFP4 recipes (the e2m1 weights with a
+ * scale per 32 or 16 input channels, as the moe_weights_t comment lists them).
+ * The routed-expert GEMMs read each weight row's scales 256 input channels at a
+ * time for 32 rows at once; in the row-major layout those bytes lie scattered
+ * over 32 cache lines that are fetched again for every 256 channels.  The packed
+ * layout puts them together:
+ *   for each block b of 32 consecutive rows, each s = 0 .. row_len/256 - 1 and
+ *   each row r of the block: the R = 256/G scale bytes of row 32b + r for input
+ *   channels 256s .. 256s+255, at byte ((b * (row_len/256) + s) * 32 + r) * R.
+ * The packed array has the same size as the row-major one.
+ *   recipe:  MOE_RECIPE_MXFP4 (G = 32, E8M0 bytes) or MOE_RECIPE_NVFP4 (G = 16,
+ *            e4m3fn codes); anything else is MOE_ERR_INVALID_ARGUMENT.
+ *   rows:    weight rows of the matrix, all experts stacked (n*2I for w13,
+ *            n*H for w2); a multiple of 32, else MOE_ERR_UNSUPPORTED.
+ *   row_len: input channels of a row (H for w13, I for w2); a multiple of 256,
+ *            else MOE_ERR_UNSUPPORTED.
+ *   src:     device, row-major [rows][row_len/G] bytes; dst: device, same size.
+ *            Both 16-byte aligned and not overlapping (else
+ *            MOE_ERR_INVALID_ARGUMENT); dst is fully overwritten.
+ * rows == 0 returns MOE_OK and enqueues nothing. */
+moe_status_t moe_pack_fp4_scales(int32_t recipe, int64_t rows, int32_t row_len, const void* src,
+                                 void* dst, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* moe_status_string(moe_status_t status);

@@ -14,8 +14,8 @@ RECIPE_F32, RECIPE_BF16, RECIPE_FP8_B128, RECIPE_MXFP4, RECIPE_NVFP4 = range(5)
 SCORE_SIGMOID, SCORE_SQRTSOFTPLUS = range(2)
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
-           "moe_forward", "moe_rmsnorm", "moe_forward_residual", "moe_status_string", "moe_profile_start",
-           "moe_profile_stop", "moe_kernel_tag_name")
+           "moe_forward", "moe_rmsnorm", "moe_forward_residual", "moe_pack_fp4_scales", "moe_status_string",
+           "moe_profile_start", "moe_profile_stop", "moe_kernel_tag_name")
 KERNEL_TAGS = ("gate_logits", "router", "perm_hist", "perm_scan", "perm_scatter", "gather", "tile_list",
                "ffn_gate_up", "ffn_down", "shared_gate_up", "shared_down_combine", "combine", "rmsnorm")
 
@@ -63,12 +63,13 @@ def load() -> ctypes.CDLL:
     lib.moe_forward.argtypes = [cfgp, vp, vp, vp, wp, wp, vp, vp, vp, vp, sz, vp]
     lib.moe_rmsnorm.argtypes = [cfgp, vp, vp, ctypes.c_float, vp, vp]
     lib.moe_forward_residual.argtypes = [cfgp, vp, vp, ctypes.c_float, vp, vp, wp, wp, vp, vp, vp, vp, sz, vp]
+    lib.moe_pack_fp4_scales.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
     lib.moe_profile_start.argtypes = [ctypes.c_int32]
     lib.moe_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), ctypes.c_int32]
     lib.moe_kernel_tag_name.argtypes = [ctypes.c_int32]
     lib.moe_kernel_tag_name.restype = ctypes.c_char_p
     for name in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_rmsnorm",
-                 "moe_forward_residual", "moe_profile_start", "moe_profile_stop"):
+                 "moe_forward_residual", "moe_pack_fp4_scales", "moe_profile_start", "moe_profile_stop"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -101,7 +102,33 @@ def _check(status: int, what: str):
 
 
 def make_weights(w13, w2, w13_scale=None, w2_scale=None) -> MoeWeights:
+    """Pointers as they are (fp4 scales must already be in the packed layout)."""
     return MoeWeights(_ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale))
+
+
+def moe_pack_fp4_scales(recipe, rows, row_len, src, dst, stream=None):
+    _check(load().moe_pack_fp4_scales(int(recipe), int(rows), int(row_len), _ptr(src), _ptr(dst), _stream(stream)),
+           "moe_pack_fp4_scales")
+
+
+def pack_fp4_scales(recipe, scale, stream=None):
+    """Row-major fp4 scales [n][rows][row_len/G] (uint8) -> a new tensor in the packed layout."""
+    g = 32 if recipe == RECIPE_MXFP4 else 16
+    out = scale.new_empty(scale.shape)
+    moe_pack_fp4_scales(recipe, scale.numel() // scale.shape[-1], scale.shape[-1] * g, scale.contiguous(), out, stream)
+    return out
+
+
+def make_expert_weights(recipe, w13, w2, w13_scale=None, w2_scale=None, stream=None) -> MoeWeights:
+    """Routed-expert weights as the layer call reads them.  MXFP4 / NVFP4 scales
+    (row-major, as quantised) are packed into new device tensors once, here; the
+    returned struct keeps them alive."""
+    if recipe in (RECIPE_MXFP4, RECIPE_NVFP4):
+        w13_scale = pack_fp4_scales(recipe, w13_scale, stream)
+        w2_scale = pack_fp4_scales(recipe, w2_scale, stream)
+    wts = make_weights(w13, w2, w13_scale, w2_scale)
+    wts._keep = (w13, w2, w13_scale, w2_scale)
+    return wts
 
 
 def moe_workspace_bytes(cfg: MoeConfig) -> int:

@@ -39,6 +39,7 @@
 // has left L2 and is fetched again.
 // The SwiGLU output h is written as bf16, or re-quantised to the activation format
 // (NVFP4: stored as fp16 values).
+#include <algorithm>
 #include <cstdlib>
 #include <type_traits>
 
@@ -120,6 +121,36 @@ __device__ __forceinline__ f16x8 e2m1x8_to_f16(uint32_t w, NvScale sc) {
 
 __device__ __forceinline__ i32x8 rs_cat(uint4 lo, uint4 hi) {
   return i32x8{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+}
+
+// Packed fp4 weight-scale layout: for each block of 32 consecutive weight rows and
+// each 256 input channels, the 32 rows' 256/G scale bytes (G = 32 for MXFP4, 16 for
+// NVFP4) are stored row after row.  Byte offset of scale group kg (channels
+// G*kg .. G*kg+G-1) of weight row `row` in a matrix whose rows hold rowlen channels
+// (a multiple of 256; the matrix's row count a multiple of 32).
+template <int G>
+__host__ __device__ __forceinline__ size_t fp4_scale_offset(size_t row, int rowlen, int kg) {
+  constexpr int SPR = 256 / G;                     // scale bytes of one row per 256 channels
+  return ((row >> 5) * size_t(rowlen / 256) + size_t(kg / SPR)) * (32 * SPR) + (row & 31) * SPR + kg % SPR;
+}
+
+// One thread per (weight row, 256 channels): the row's SPR bytes from the row-major
+// [rows][rowlen/G] layout into the packed one.  Threads run in packed order so the
+// stores are contiguous.
+template <int G>
+__global__ __launch_bounds__(256) void pack_fp4_scales_kernel(const uint8_t* __restrict__ src,
+                                                              uint8_t* __restrict__ dst, int64_t rows, int rowlen) {
+  constexpr int SPR = 256 / G;
+  using V = std::conditional_t<SPR == 8, uint2, uint4>;
+  const int nst = rowlen / 256;
+  const int64_t n = rows * nst;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t blk = i >> 5, r = i & 31, rb = blk / nst;
+    const int st = int(blk - rb * nst);
+    const int64_t row = rb * 32 + r;
+    const V v = *reinterpret_cast<const V*>(src + row * (rowlen / G) + size_t(st) * SPR);
+    *reinterpret_cast<V*>(dst + fp4_scale_offset<G>(size_t(row), rowlen, st * SPR)) = v;
+  }
 }
 
 }  // namespace
@@ -220,18 +251,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     return S[(size_t(sub) * (g.N / 128) + cb) * (ns / 128) + (k0 % ns) / 128];
   };
   // fp4 weight scales of fragment f at k0 for this lane's half of the stage: MX
-  // E8M0 per 32 (groups k0/32 + (KS/64)h ..), NVFP4 e4m3 per 16 (k0/16 + 8h .. +7)
-  auto bscale_fp4 = [&](int f, int k0) -> SbT {
+  // E8M0 per 32 (groups k0/32 + (KS/64)h ..), NVFP4 e4m3 per 16 (k0/16 + 8h .. +7),
+  // in the packed layout (fp4_scale_offset): a wave's 32 rows read one contiguous
+  // run of whole lines per stage.  Per lane a fixed base; the stage adds a
+  // wave-uniform offset.
+  const uint8_t* sb_base[2];
+  if constexpr (FP4) {
     const uint8_t* S = static_cast<const uint8_t*>(g.B_scale);
-    const uint8_t* p;
-    if (MODE == EPI_SWIGLU) {
-      p = S + (size_t(sub0) * 2 * ns + ncol[f]) * (K / SG) + k0 / SG;
-    } else {
-      const int sub = ti.e * g.n_experts_split + k0 / ns;
-      p = S + (size_t(sub) * g.N + ncol[f]) * (ns / SG) + (k0 % ns) / SG;
-    }
-    return *reinterpret_cast<const SbT*>(p + half * (KS / SG / 2));
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+      sb_base[f] = S + (MODE == EPI_SWIGLU
+                            ? fp4_scale_offset<SG>(size_t(sub0) * 2 * ns + ncol[f], K, half * (KS / SG / 2))
+                            : fp4_scale_offset<SG>(size_t(ti.e) * g.n_experts_split * g.N + ncol[f], ns,
+                                                   half * (KS / SG / 2)));
+  }
+  auto bscale_fp4 = [&](int f, int k0) -> SbT {
+    constexpr int RUN = 32 * 256 / SG;             // bytes of one 32-row block per 256 channels
+    size_t off;
+    if (MODE == EPI_SWIGLU) off = size_t(k0 / 256) * RUN + (k0 % 256) / SG;
+    else off = size_t(k0 / ns) * g.N * (ns / SG) + size_t((k0 % ns) / 256) * RUN + (k0 % 256) / SG;
+    return *reinterpret_cast<const SbT*>(sb_base[f] + off);
   };
+
 
   // ---- activation copies: copy j of wave w fills LDS chunk positions (w*MS + j)*64 + lane
   std::conditional_t<BUF, uint32_t, const uint8_t*> a_src[A_INSTR];
@@ -642,6 +683,16 @@ hipError_t launch_rs_swiglu(int recipe, int ms, int m_tiles, const GemmArgs& g, 
 // each, an integer), see GemmArgs::split_stride.
 hipError_t launch_rs_down(int recipe, int ms, int m_tiles, const GemmArgs& g, hipStream_t st, int ksplit) {
   return rs_launch_recipe<EPI_STORE>(recipe, ms, dim3((g.N + RS_NB - 1) / RS_NB, m_tiles, ksplit), g, st);
+}
+
+hipError_t launch_pack_fp4_scales(int recipe, int64_t rows, int rowlen, const void* src, void* dst, hipStream_t st) {
+  const int64_t n = rows * (rowlen / 256);
+  const int grid = int(std::min<int64_t>((n + 255) / 256, 65536));
+  const uint8_t* s = static_cast<const uint8_t*>(src);
+  uint8_t* d = static_cast<uint8_t*>(dst);
+  if (recipe == MOE_RECIPE_MXFP4) pack_fp4_scales_kernel<32><<<grid, 256, 0, st>>>(s, d, rows, rowlen);
+  else pack_fp4_scales_kernel<16><<<grid, 256, 0, st>>>(s, d, rows, rowlen);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -59,6 +59,10 @@ hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32
                           const void* x, const moe_weights_t* shared, const void* resid, void* out, void* h_shared,
                           float* sh_out, float* sh_part, hipStream_t st);
 
+// MXFP4 / NVFP4 weight scales from the row-major [rows][rowlen/G] layout into the packed
+// one the register-streaming kernels read (rows % 32 == 0, rowlen % 256 == 0).
+hipError_t launch_pack_fp4_scales(int recipe, int64_t rows, int rowlen, const void* src, void* dst, hipStream_t st);
+
 hipError_t launch_rmsnorm(const moe_config_t& c, const void* h, const float* w, float eps, void* x, hipStream_t st);
 
 }  // namespace moe

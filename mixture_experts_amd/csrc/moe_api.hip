@@ -578,4 +578,18 @@ moe_status_t moe_forward_residual(const moe_config_t* cfg, const void* resid, co
   return to_status(e);
 }
 
+moe_status_t moe_pack_fp4_scales(int32_t recipe, int64_t rows, int32_t row_len, const void* src, void* dst,
+                                 void* stream) {
+  if (recipe != MOE_RECIPE_MXFP4 && recipe != MOE_RECIPE_NVFP4) return MOE_ERR_INVALID_ARGUMENT;
+  if (rows < 0 || row_len <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (rows % 32 != 0 || row_len % 256 != 0) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!src || !dst || !aligned16(src) || !aligned16(dst)) return MOE_ERR_INVALID_ARGUMENT;
+  const int64_t bytes = rows * (row_len / (recipe == MOE_RECIPE_MXFP4 ? 32 : 16));
+  const char* s = static_cast<const char*>(src);
+  const char* d = static_cast<const char*>(dst);
+  if (s < d + bytes && d < s + bytes) return MOE_ERR_INVALID_ARGUMENT;   // overlapping buffers
+  return to_status(launch_pack_fp4_scales(recipe, rows, row_len, src, dst, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -56,7 +56,7 @@ def rel_l2(got: np.ndarray, want: np.ndarray) -> float:
 
 
 def weights(inp: G.MoEInputs):
-    ex = M.make_weights(inp.w13, inp.w2, inp.w13_scale, inp.w2_scale)
+    ex = M.make_expert_weights(inp.cfg.recipe, inp.w13, inp.w2, inp.w13_scale, inp.w2_scale)
     sh = M.make_weights(inp.shared_w13, inp.shared_w2) if inp.cfg.num_shared > 0 else None
     return ex, sh
 

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "moe.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
@@ -103,3 +103,22 @@ def test_zero_tokens_is_a_no_op():
     lib = M.load()
     cfg = M.make_config(C.TINY_F32.replace(num_tokens=0))
     assert lib.moe_forward(ctypes.byref(cfg), None, None, None, None, None, None, None, None, None, 0, None) == 0
+
+
+@pytest.mark.parametrize("recipe,rows,row_len,src,dst,want", [
+    (M.RECIPE_BF16, 32, 256, 1 << 20, 1 << 24, 1),           # only the fp4 recipes have packed scales
+    (M.RECIPE_FP8_B128, 32, 256, 1 << 20, 1 << 24, 1),
+    (M.RECIPE_MXFP4, -32, 256, 1 << 20, 1 << 24, 1),
+    (M.RECIPE_MXFP4, 32, 0, 1 << 20, 1 << 24, 1),
+    (M.RECIPE_MXFP4, 48, 256, 1 << 20, 1 << 24, 2),          # rows not a multiple of 32
+    (M.RECIPE_NVFP4, 32, 384, 1 << 20, 1 << 24, 2),          # row length not a multiple of 256
+    (M.RECIPE_MXFP4, 32, 256, None, 1 << 24, 1),
+    (M.RECIPE_NVFP4, 32, 256, (1 << 20) + 8, 1 << 24, 1),    # misaligned
+    (M.RECIPE_MXFP4, 64, 1024, 1 << 20, (1 << 20) + 1024, 1),  # 1 KiB apart: the 2 KiB arrays overlap
+    (M.RECIPE_MXFP4, 0, 256, None, None, 0),                 # no rows: a no-op
+])
+def test_pack_fp4_scales_argument_checks(recipe, rows, row_len, src, dst, want):
+    """Rejected before anything is enqueued (the pointers are never dereferenced)."""
+    lib = M.load()
+    p = lambda a: None if a is None else ctypes.c_void_p(a)
+    assert lib.moe_pack_fp4_scales(recipe, rows, row_len, p(src), p(dst), None) == want
