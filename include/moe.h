@@ -22,7 +22,9 @@
  *                      residual added in the combine;
  *   moe_pack_fp4_scales - weight preparation (once per set of weights, outside
  *                      the layer call): MXFP4 / NVFP4 weight scales into the
- *                      packed layout the routed-expert GEMMs read.
+ *                      packed layout the routed-expert GEMMs read;
+ *   moe_convert_mxfp4_to_fp8 - weight preparation: MXFP4 weights into the
+ *                      fp8 recipe's format (DeepSeek-V4-Pro overview, convert.py).
  *
  * Conventions for every entry point
  *   - Every buffer pointer is a DEVICE pointer owned by the caller; the library
@@ -41,10 +43,6 @@
  *     MOE_ERR_WORKSPACE_TOO_SMALL.  MOE_ERR_LAUNCH reports a failed kernel
  *     launch.  Faults inside kernels surface at the caller's next
  *     synchronisation.  num_tokens == 0 returns MOE_OK and enqueues nothing.
- *   - Environment: MOE_LDS_FLAT (any value) makes the GEMM kernels copy
- *     activations and weights into LDS with 64-bit addresses even where the
- *     tensors fit 32-bit buffer offsets (the faster form).  Results are the
- *     same either way; the switch exists to test the 64-bit form.
  *   - Matrices are row-major.  Weights use the [out, in] convention of the
  *     checkpoints (the gate matrix is [E, H], 384 x 7168 in the walk-through).
  *
@@ -260,6 +258,29 @@ moe_status_t moe_forward_residual(const moe_config_t* cfg, const void* resid, co
  * rows == 0 returns MOE_OK and enqueues nothing. */
 moe_status_t moe_pack_fp4_scales(int32_t recipe, int64_t rows, int32_t row_len, const void* src,
                                  void* dst, void* stream);
+
+/* Weight conversion MXFP4 -> MOE_RECIPE_FP8_B128 weights (the DeepSeek-V4-Pro
+ * overview, lzwjava.github.io, convert.py entry: FP4 e2m1fn to FP8 e4m3fn without
+ * loss, with care for the scales).  Run once per set of weights, outside the
+ * layer call, on each matrix (w13 with rows = n*2I, row_len = H; w2 with rows =
+ * n*H, row_len = I).
+ *   w_fp4:   device, packed e2m1 [rows][row_len/2] (low nibble = even column);
+ *   w_e8m0:  device, E8M0 bytes [rows][row_len/32], ROW-MAJOR (the layout before
+ *            moe_pack_fp4_scales; bytes 0xFF, E8M0's NaN, are not supported);
+ *   w_fp8:   device, out: e4m3fn codes [rows][row_len];
+ *   w_fp8_scale: device, out: fp32 [rows/128][row_len/128], one per 128 x 128 block;
+ *   inexact_blocks: device int32 or NULL; out: the number of blocks not reproduced
+ *            exactly.
+ * Block B's scale is 2^(E - 127), E the largest E8M0 byte of B's groups; an element
+ * with group byte b and e2m1 value q becomes e4m3(q * 2^(b - E)), rounding to
+ * nearest with ties to the even code.  Every e2m1 value is an e4m3 value, so a block
+ * whose groups' exponents lie within 8 of E is exact (0.5 * 2^-8 is e4m3's smallest
+ * subnormal); others lose the values that fall below that and are counted.
+ * rows and row_len must be multiples of 128 (else MOE_ERR_UNSUPPORTED); w_fp4, w_fp8,
+ * w_fp8_scale and w_e8m0 16-byte aligned, inexact_blocks 4-byte aligned (else
+ * MOE_ERR_INVALID_ARGUMENT).  rows == 0 returns MOE_OK and enqueues nothing. */
+moe_status_t moe_convert_mxfp4_to_fp8(int64_t rows, int32_t row_len, const void* w_fp4, const void* w_e8m0,
+                                      void* w_fp8, float* w_fp8_scale, int32_t* inexact_blocks, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* moe_status_string(moe_status_t status);

@@ -3,19 +3,22 @@ every step of the layer runs in the library's HIP kernels.  Tensors are torch
 device tensors; the stream is torch's current HIP stream unless given."""
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+# The same library with the GEMM kernels' 64-bit LDS-copy form forced on (tests only).
+FLAT_LIB_PATH = os.path.join(_HERE, "libmoe_mi355x_flatcopy.so")
 
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_LAUNCH = range(5)
 RECIPE_F32, RECIPE_BF16, RECIPE_FP8_B128, RECIPE_MXFP4, RECIPE_NVFP4 = range(5)
 SCORE_SIGMOID, SCORE_SQRTSOFTPLUS = range(2)
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
-           "moe_forward", "moe_rmsnorm", "moe_forward_residual", "moe_pack_fp4_scales", "moe_status_string",
-           "moe_profile_start", "moe_profile_stop", "moe_kernel_tag_name")
+           "moe_forward", "moe_rmsnorm", "moe_forward_residual", "moe_pack_fp4_scales", "moe_convert_mxfp4_to_fp8",
+           "moe_status_string", "moe_profile_start", "moe_profile_stop", "moe_kernel_tag_name")
 KERNEL_TAGS = ("gate_logits", "router", "perm_hist", "perm_scan", "perm_scatter", "gather", "tile_list",
                "ffn_gate_up", "ffn_down", "shared_gate_up", "shared_down_combine", "combine", "rmsnorm")
 
@@ -39,16 +42,23 @@ class MoeError(RuntimeError):
 
 
 _lib = None
+_loaded = {}
 
 
-def load() -> ctypes.CDLL:
-    """Load the HIP library; raises if it has not been built (there is no fallback)."""
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load the HIP library; raises if it has not been built (there is no fallback).
+    Without `path`: the library every call goes through (libmoe_mi355x.so unless
+    `library()` has switched it)."""
     global _lib
-    if _lib is not None:
+    if path is None:
+        if _lib is None:
+            _lib = load(LIB_PATH)
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m mixture_experts_amd.build`")
-    lib = ctypes.CDLL(LIB_PATH)
+    if path in _loaded:
+        return _loaded[path]
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m mixture_experts_amd.build`")
+    lib = ctypes.CDLL(path)
     vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     cfgp = ctypes.POINTER(MoeConfig)
     wp = ctypes.POINTER(MoeWeights)
@@ -64,15 +74,30 @@ def load() -> ctypes.CDLL:
     lib.moe_rmsnorm.argtypes = [cfgp, vp, vp, ctypes.c_float, vp, vp]
     lib.moe_forward_residual.argtypes = [cfgp, vp, vp, ctypes.c_float, vp, vp, wp, wp, vp, vp, vp, vp, sz, vp]
     lib.moe_pack_fp4_scales.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
+    lib.moe_convert_mxfp4_to_fp8.argtypes = [ctypes.c_int64, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
     lib.moe_profile_start.argtypes = [ctypes.c_int32]
     lib.moe_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), ctypes.c_int32]
     lib.moe_kernel_tag_name.argtypes = [ctypes.c_int32]
     lib.moe_kernel_tag_name.restype = ctypes.c_char_p
     for name in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_rmsnorm",
-                 "moe_forward_residual", "moe_pack_fp4_scales", "moe_profile_start", "moe_profile_stop"):
+                 "moe_forward_residual", "moe_pack_fp4_scales", "moe_convert_mxfp4_to_fp8", "moe_profile_start",
+                 "moe_profile_stop"):
         getattr(lib, name).restype = i32
-    _lib = lib
+    _loaded[path] = lib
     return lib
+
+
+@contextlib.contextmanager
+def library(path: str):
+    """Route every call of this module through another build of the library while
+    the context is open (the tests' FLAT-copy build)."""
+    global _lib
+    saved = _lib
+    _lib = load(path)
+    try:
+        yield _lib
+    finally:
+        _lib = saved
 
 
 def make_config(cfg) -> MoeConfig:
@@ -117,6 +142,15 @@ def pack_fp4_scales(recipe, scale, stream=None):
     out = scale.new_empty(scale.shape)
     moe_pack_fp4_scales(recipe, scale.numel() // scale.shape[-1], scale.shape[-1] * g, scale.contiguous(), out, stream)
     return out
+
+
+def moe_convert_mxfp4_to_fp8(w_fp4, w_e8m0, w_fp8, w_fp8_scale, inexact_blocks=None, stream=None):
+    """MXFP4 [rows][row_len/2] + row-major E8M0 [rows][row_len/32] -> e4m3fn codes
+    [rows][row_len] + fp32 scales [rows/128][row_len/128] (include/moe.h)."""
+    rows = w_fp4.numel() // w_fp4.shape[-1]
+    _check(load().moe_convert_mxfp4_to_fp8(int(rows), int(w_fp4.shape[-1] * 2), _ptr(w_fp4), _ptr(w_e8m0),
+                                           _ptr(w_fp8), _ptr(w_fp8_scale), _ptr(inexact_blocks), _stream(stream)),
+           "moe_convert_mxfp4_to_fp8")
 
 
 def make_expert_weights(recipe, w13, w2, w13_scale=None, w2_scale=None, stream=None) -> MoeWeights:

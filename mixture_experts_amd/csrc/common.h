@@ -6,6 +6,13 @@
 
 #include "../../include/moe.h"
 
+// 1: the GEMM kernels copy activations and weights into LDS with 64-bit (FLAT)
+// addresses even where 32-bit buffer offsets would do.  The production library is
+// built with 0; a second build with 1 lets the tests exercise the 64-bit form.
+#ifndef MOE_FORCE_FLAT_COPIES
+#define MOE_FORCE_FLAT_COPIES 0
+#endif
+
 namespace moe {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;

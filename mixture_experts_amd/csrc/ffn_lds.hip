@@ -38,8 +38,6 @@
 // activation block meet in that XCD's L2.  The row tiles of one expert read the
 // same weight rows, but far apart in time, so each of them streams the weights
 // from HBM again; experts of 257..511 rows therefore pay two weight passes.
-#include <cstdlib>
-
 #include "gemm_common.h"
 #include "kernels.h"
 
@@ -208,12 +206,12 @@ __device__ __forceinline__ void stage_fp8(f32x4 (&acc)[MU][NC], const uint8_t* A
   }
 }
 
-// MS: 32-row fragments per tile; WM x WN: wavefront grid; PIPE (bf16 only): 1 =
+// MS: 32-row fragments per tile; WM x WN: wavefront grid; PIPE (bf16 only): 2 =
 // the stage barrier sits before the stage's last sub-step, so that stage k+2's
-// copies and stage k+1's first LDS reads overlap stage k's last MFMAs; 2 = the
-// same with three weight slots (and two activation slots), so that each
-// stage's weight copies have two stages of compute to land; NB: weight rows per
-// tile (SwiGLU: NB/2 h columns).
+// copies and stage k+1's first LDS reads overlap stage k's last MFMAs, with three
+// weight slots (and two activation slots), so that each stage's weight copies
+// have two stages of compute to land; 0 = one stage in flight (fp8); NB: weight
+// rows per tile (SwiGLU: NB/2 h columns).
 template <int MS, int MODE, int KIND, int WM, int WN, int PIPE, int NB, bool BUF>
 __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
   constexpr int NW = WM * WN;                       // wavefronts
@@ -511,73 +509,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
     else if (MW >= 2 && nj == 2) mainloop(std::integral_constant<int, (MW >= 2 ? 2 : 0)>{});
     else if (nj == 1) mainloop(std::integral_constant<int, 1>{});
     else mainloop(std::integral_constant<int, 0>{});
-  } else if constexpr (PIPE == 1 && !FP8) {
-    // ---- bf16 main loop, barrier before the last sub-step.  Every wave runs it,
-    // also one without real rows (its copies and barriers are shared).
-    constexpr int NS = ROWB / 32;
-    const int half = lane >> 5, l32 = lane & 31;
-    auto mainloop = [&](auto njc) {
-      constexpr int NJ = decltype(njc)::value;
-      constexpr int NJA = NJ > 0 ? NJ : 1;
-      bf16x8 bv[2][NF], av[2][NJA];
-      auto rd = [&](auto bufc, int s, int slot) {
-        constexpr int bb = decltype(bufc)::value;
-        if constexpr (NJ > 0) {
-          const int off = l32 * ROWB + (swz_slot(l32, 2 * s + half) << 4);
-          const uint8_t* Aw = (bb == 0 ? As0 : As1) + wm * 32 * ROWB + off;
-          const uint8_t* Bw = (bb == 0 ? Bs0 : Bs1) + brow0 * ROWB + off;
-#pragma unroll
-          for (int f = 0; f < NF; ++f) bv[slot][f] = __builtin_bit_cast(bf16x8, lds16(Bw + bfrag_row<SPLIT, NB>(f) * ROWB));
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) av[slot][j] = __builtin_bit_cast(bf16x8, lds16(Aw + WM * 32 * ROWB * j));
-        }
-      };
-      auto mm = [&](int slot) {
-        if constexpr (NJ > 0) {
-#pragma unroll
-          for (int j = 0; j < NJ; ++j)
-#pragma unroll
-            for (int f = 0; f < NF; ++f)
-              acc16[j][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[slot][f], av[slot][j], acc16[j][f], 0, 0, 0);
-        }
-      };
-      // stage kt from slot bb; stage kt+1 is landing in the other slot
-      auto step = [&](int kt, auto bufc) {
-        constexpr int bb = decltype(bufc)::value;
-#pragma unroll
-        for (int s = 0; s < NS - 1; ++s) {
-          rd(bufc, s + 1, (s + 1) & 1);
-          sched_fence();
-          mm(s & 1);
-          sched_fence();
-        }
-        if (kt + 1 < KT) {
-          wait_vmcnt<0>();                            // stage kt+1 has landed (own copies)
-          __syncthreads();                            // (everyone's); everyone is done reading stage kt
-          if (kt + 2 < KT) issue((kt + 2) * KS, bb);
-        }
-        rd(std::integral_constant<int, bb ^ 1>{}, 0, 0);   // (after the last stage: unused)
-        sched_fence();
-        mm((NS - 1) & 1);
-        sched_fence();
-      };
-      rd(std::integral_constant<int, 0>{}, 0, 0);
-      int kt = 0;
-      for (; kt + 1 < KT; kt += 2) {
-        step(kt, std::integral_constant<int, 0>{});
-        step(kt + 1, std::integral_constant<int, 1>{});
-      }
-      if (kt < KT) step(kt, std::integral_constant<int, 0>{});
-    };
-    issue(0, 0);
-    if (KT > 1) issue(KS, 1);
-    wait_vmcnt<0>();                                // (a wave's copy count varies with the tile's rows)
-    __syncthreads();
-    if (MW >= 4 && nj == 4) mainloop(std::integral_constant<int, (MW >= 4 ? 4 : 0)>{});
-    else if (MW >= 3 && nj == 3) mainloop(std::integral_constant<int, (MW >= 3 ? 3 : 0)>{});
-    else if (MW >= 2 && nj == 2) mainloop(std::integral_constant<int, (MW >= 2 ? 2 : 0)>{});
-    else if (nj == 1) mainloop(std::integral_constant<int, 1>{});
-    else mainloop(std::integral_constant<int, 0>{});
   } else {
   // ---- main loop: stage kt is consumed from slot kt % NST while stage kt+1 lands
 #pragma unroll
@@ -732,45 +663,40 @@ void launch_lds_variant(const GemmArgs& g, int m_tiles, hipStream_t st) {
   ffn_lds_kernel<MS, MODE, KIND, WM, WN, PIPE, NB, BUF><<<dim3(ncols, m_tiles), 64 * WM * WN, 0, st>>>(g);
 }
 
-// Production configurations.  bf16: 256-row tiles on 2 x 4 wavefronts (two per
-// SIMD) with the stage barrier before the last sub-step and a three-slot weight
-// ring (all 160 KB of LDS); smaller tiles on 2 x 2 wavefronts.  fp8: 2 x 4 wavefronts, 256-row tiles: the block-scale FMAs keep
-// the accumulators in ordinary VGPRs, and a second wave per SIMD overlaps one
-// wave's FMAs with the other's MFMAs.
+// Production configurations: 256-row tiles on 2 x 4 wavefronts (two per SIMD).
+// bf16: the stage barrier before the last sub-step and a three-slot weight ring
+// (all 160 KB of LDS).  fp8: the block-scale FMAs keep the accumulators in ordinary
+// VGPRs, and a second wave per SIMD overlaps one wave's FMAs with the other's MFMAs.
 template <int MODE, int KIND, bool BUF>
-static hipError_t launch_lds_ms(int ms, int m_tiles, const GemmArgs& g, hipStream_t st) {
-  if constexpr (KIND == KIND_FP8) {
-    if (ms <= 4) launch_lds_variant<4, MODE, KIND, BUF, 2, 4>(g, m_tiles, st);
-    else launch_lds_variant<8, MODE, KIND, BUF, 2, 4>(g, m_tiles, st);
-  } else {
-    if (ms <= 2) launch_lds_variant<2, MODE, KIND, BUF, 2, 2>(g, m_tiles, st);
-    else if (ms <= 4) launch_lds_variant<4, MODE, KIND, BUF, 2, 2>(g, m_tiles, st);
-    else launch_lds_variant<8, MODE, KIND, BUF, 2, 4, 2>(g, m_tiles, st);
-  }
+static hipError_t launch_lds_tiles(int m_tiles, const GemmArgs& g, hipStream_t st) {
+  if constexpr (KIND == KIND_FP8) launch_lds_variant<8, MODE, KIND, BUF, 2, 4>(g, m_tiles, st);
+  else launch_lds_variant<8, MODE, KIND, BUF, 2, 4, 2>(g, m_tiles, st);
   return hipGetLastError();
 }
 
 // Buffer-descriptor copies address A and the tile's expert weights with 32-bit
-// offsets: usable when a_rows is known and both extents stay below 4 GiB.  The
-// environment variable MOE_LDS_FLAT forces the FLAT-copy form (to test it).
+// offsets: usable when a_rows is known and both extents stay below 4 GiB.  A
+// library built with MOE_FORCE_FLAT_COPIES=1 always takes the 64-bit FLAT-copy form
+// (the test build exercises it; no shape of the test workloads reaches it otherwise).
 template <int MODE, int KIND>
-static hipError_t launch_lds_any(int ms, int m_tiles, const GemmArgs& g, hipStream_t st) {
+static hipError_t launch_lds_any(int m_tiles, const GemmArgs& g, hipStream_t st) {
   constexpr int64_t eb = KIND == KIND_FP8 ? 1 : 2, lim = (int64_t(1) << 32) - 256;
   const int64_t a_bytes = g.a_rows * g.lda * eb;
   const int64_t b_bytes = MODE == EPI_SWIGLU ? 2 * int64_t(g.nsplit) * g.K * eb
                                              : int64_t(g.n_experts_split) * g.N * g.nsplit * eb;
-  if (g.a_rows > 0 && a_bytes < lim && b_bytes < lim && std::getenv("MOE_LDS_FLAT") == nullptr)
-    return launch_lds_ms<MODE, KIND, true>(ms, m_tiles, g, st);
-  return launch_lds_ms<MODE, KIND, false>(ms, m_tiles, g, st);
+  if (!MOE_FORCE_FLAT_COPIES && g.a_rows > 0 && a_bytes < lim && b_bytes < lim)
+    return launch_lds_tiles<MODE, KIND, true>(m_tiles, g, st);
+  return launch_lds_tiles<MODE, KIND, false>(m_tiles, g, st);
 }
 
-hipError_t launch_lds_swiglu(bool fp8, int ms, int m_tiles, const GemmArgs& g, hipStream_t st) {
-  return fp8 ? launch_lds_any<EPI_SWIGLU, KIND_FP8>(ms, m_tiles, g, st)
-             : launch_lds_any<EPI_SWIGLU, KIND_BF16>(ms, m_tiles, g, st);
+// 256-row tiles (see launch_lds_tiles).
+hipError_t launch_lds_swiglu(bool fp8, int m_tiles, const GemmArgs& g, hipStream_t st) {
+  return fp8 ? launch_lds_any<EPI_SWIGLU, KIND_FP8>(m_tiles, g, st)
+             : launch_lds_any<EPI_SWIGLU, KIND_BF16>(m_tiles, g, st);
 }
-hipError_t launch_lds_down(bool fp8, int ms, int m_tiles, const GemmArgs& g, hipStream_t st) {
-  return fp8 ? launch_lds_any<EPI_STORE, KIND_FP8>(ms, m_tiles, g, st)
-             : launch_lds_any<EPI_STORE, KIND_BF16>(ms, m_tiles, g, st);
+hipError_t launch_lds_down(bool fp8, int m_tiles, const GemmArgs& g, hipStream_t st) {
+  return fp8 ? launch_lds_any<EPI_STORE, KIND_FP8>(m_tiles, g, st)
+             : launch_lds_any<EPI_STORE, KIND_BF16>(m_tiles, g, st);
 }
 
 }  // namespace moe

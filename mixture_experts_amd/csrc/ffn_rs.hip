@@ -40,7 +40,6 @@
 // The SwiGLU output h is written as bf16, or re-quantised to the activation format
 // (NVFP4: stored as fp16 values).
 #include <algorithm>
-#include <cstdlib>
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -651,13 +650,13 @@ static void rs_launch_t(int ms, dim3 grid, const GemmArgs& g, hipStream_t st) {
 
 // The fp4 recipes copy activations through buffer descriptors when A's extent
 // (a_rows known) is below 4 GiB (measured: MXFP4 gate/up 2.37 -> 2.18 ms; bf16
-// decode was slower that way, 3.19 -> 3.66 ms, and keeps the FLAT form).
-// MOE_LDS_FLAT forces the FLAT form.
+// decode was slower that way, 3.19 -> 3.66 ms, and keeps the FLAT form).  A
+// library built with MOE_FORCE_FLAT_COPIES=1 always takes the FLAT form.
 template <int MODE, int RECIPE>
 static void rs_launch(int ms, dim3 grid, const GemmArgs& g, hipStream_t st) {
   if constexpr (RECIPE == MOE_RECIPE_MXFP4 || RECIPE == MOE_RECIPE_NVFP4) {
     constexpr int64_t ea = RECIPE == MOE_RECIPE_NVFP4 ? 2 : 1;
-    if (g.a_rows > 0 && g.a_rows * g.lda * ea < (int64_t(1) << 32) - 256 && std::getenv("MOE_LDS_FLAT") == nullptr) {
+    if (!MOE_FORCE_FLAT_COPIES && g.a_rows > 0 && g.a_rows * g.lda * ea < (int64_t(1) << 32) - 256) {
       rs_launch_t<MODE, RECIPE, true>(ms, grid, g, st);
       return;
     }

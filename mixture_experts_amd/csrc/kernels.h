@@ -63,6 +63,11 @@ hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32
 // one the register-streaming kernels read (rows % 32 == 0, rowlen % 256 == 0).
 hipError_t launch_pack_fp4_scales(int recipe, int64_t rows, int rowlen, const void* src, void* dst, hipStream_t st);
 
+// MXFP4 weights [rows][row_len] -> e4m3fn codes with fp32 scales per 128 x 128 block
+// (rows, row_len multiples of 128); inexact (nullable) counts blocks not reproduced exactly.
+hipError_t launch_mxfp4_to_fp8(int64_t rows, int row_len, const void* q, const void* e8, void* out, float* out_scale,
+                               int32_t* inexact, hipStream_t st);
+
 hipError_t launch_rmsnorm(const moe_config_t& c, const void* h, const float* w, float eps, void* x, hipStream_t st);
 
 }  // namespace moe

@@ -19,8 +19,8 @@ hipError_t launch_swiglu_slabs(const float* part, int nz, int T, int nes, int Is
                                hipStream_t st);
 hipError_t launch_build_tiles2(const int32_t* offsets, int E, int thresh, int bm_large, int bm_small,
                                int32_t* tiles_l, int32_t* tiles_s, hipStream_t st);
-hipError_t launch_lds_swiglu(bool fp8, int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
-hipError_t launch_lds_down(bool fp8, int ms, int m_tiles, const GemmArgs& g, hipStream_t st);
+hipError_t launch_lds_swiglu(bool fp8, int m_tiles, const GemmArgs& g, hipStream_t st);   // 256-row tiles
+hipError_t launch_lds_down(bool fp8, int m_tiles, const GemmArgs& g, hipStream_t st);
 
 namespace {
 
@@ -64,6 +64,13 @@ size_t act_scale_bytes(const moe_config_t& c, int64_t rows, int64_t cols) {
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// Routed experts with quantised weights and activations.
+bool quantised(const moe_config_t& c) {
+  return c.recipe == MOE_RECIPE_FP8_B128 || c.recipe == MOE_RECIPE_MXFP4 || c.recipe == MOE_RECIPE_NVFP4;
+}
+// Quantised activations stored as codes plus a separate scale array (x_perm_scale).
+bool act_scaled(const moe_config_t& c) { return c.recipe == MOE_RECIPE_FP8_B128 || c.recipe == MOE_RECIPE_MXFP4; }
+
 int shared_ms(int T) { return T > 32 ? 2 : 1; }   // register-streaming tiles for small token counts
 
 // Shared expert at small token counts (decode): its two GEMMs have too few output
@@ -95,7 +102,7 @@ SharedSplit shared_split(const moe_config_t& c) {
 // Scratch layout; the same for every entry point so one size serves all of them.
 struct Layout {
   size_t logits, gate_partial, hist, tiles_l, tiles_s, h, h_scale, h_shared, sh_out, sh_part, idx, w, offsets, sorted,
-      pos, x_perm, x_perm_scale, y_perm, xn, total;
+      pos, xq, xq_scale, y_perm, xn, total;
 };
 
 Layout layout(const moe_config_t& c) {
@@ -122,8 +129,10 @@ Layout layout(const moe_config_t& c) {
   L.offsets = take(size_t((E + 1) * 4));
   L.sorted = take(size_t(P * 4));
   L.pos = take(size_t(P * 4));
-  L.x_perm = take(size_t(P * H) * routed_act_bytes(c));
-  L.x_perm_scale = take(act_scale_bytes(c, P, H));
+  // moe_forward's once-per-token quantised copy of x for the quantised recipes (the
+  // routed GEMMs gather its rows; moe_permute writes the caller's x_perm instead)
+  L.xq = take(quantised(c) ? size_t(T * H) * routed_act_bytes(c) : 0);
+  L.xq_scale = take(act_scale_bytes(c, T, H));
   L.y_perm = take(size_t(P * H) * act_bytes(c));
   L.xn = take(size_t(T * H) * act_bytes(c));          // normalised rows (moe_forward_residual)
   L.total = o;
@@ -144,12 +153,6 @@ moe_status_t check_common(const moe_config_t* c, void* ws, size_t ws_bytes) {
   return MOE_OK;
 }
 
-// Routed experts with quantised weights and activations.
-bool quantised(const moe_config_t& c) {
-  return c.recipe == MOE_RECIPE_FP8_B128 || c.recipe == MOE_RECIPE_MXFP4 || c.recipe == MOE_RECIPE_NVFP4;
-}
-// Quantised activations stored as codes plus a separate scale array (x_perm_scale).
-bool act_scaled(const moe_config_t& c) { return c.recipe == MOE_RECIPE_FP8_B128 || c.recipe == MOE_RECIPE_MXFP4; }
 
 bool weights_ok(const moe_config_t& c, const moe_weights_t* w) {
   if (!w || !w->w13 || !w->w2) return false;
@@ -232,7 +235,7 @@ hipError_t launch_grouped_ffn(const moe_config_t& c, const int32_t* offsets, con
     } else {
       if (fp.max_l > 0) {
         g.tiles = s.tiles_l;
-        e = launch_lds_swiglu(fp8, fp.bm_l / 32, fp.max_l, g, st);
+        e = launch_lds_swiglu(fp8, fp.max_l, g, st);
       }
       if (e == hipSuccess) {
         g.tiles = s.tiles_s;
@@ -262,7 +265,7 @@ hipError_t launch_grouped_ffn(const moe_config_t& c, const int32_t* offsets, con
   }
   if (fp.max_l > 0) {
     d.tiles = s.tiles_l;
-    e = launch_lds_down(fp8, fp.bm_l / 32, fp.max_l, d, st);
+    e = launch_lds_down(fp8, fp.max_l, d, st);
     if (e != hipSuccess) return e;
   }
   d.tiles = s.tiles_s;
@@ -323,10 +326,10 @@ hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32
     ProfScope p(MOE_K_COMBINE, st);
     return launch_combine_rows(c, y_perm, pair_pos, topk_w, sh_part, ss.ks2, resid, out, st);
   }
+  // Prefill-sized token counts (T > 256; fewer take the K split above): the
+  // LDS-staged kernel's 256-row tiles, or the fp32 kernel.
   const bool f32 = c.recipe == MOE_RECIPE_F32;
-  const bool lds = !f32 && T >= 128;                  // LDS-staged kernel for prefill-sized token counts
-  const int ms = lds ? (T >= 256 ? 8 : 4) : shared_ms(T);
-  const int BM = f32 ? 16 : ms * 32, mt = (T + BM - 1) / BM;
+  const int BM = f32 ? 16 : 256, mt = (T + BM - 1) / BM;
   GemmArgs g{};
   g.swiglu_limit = c.swiglu_limit;
   g.A = x;
@@ -342,8 +345,7 @@ hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32
   g.ldo = SI;
   {
     ProfScope p(MOE_K_SHARED_GATE_UP, st);
-    e = f32 ? launch_f32(EPI_SWIGLU, mt, g, st)
-            : (lds ? launch_lds_swiglu(false, ms, mt, g, st) : launch_rs_swiglu(MOE_RECIPE_BF16, ms, mt, g, st));
+    e = f32 ? launch_f32(EPI_SWIGLU, mt, g, st) : launch_lds_swiglu(false, mt, g, st);
   }
   if (e != hipSuccess) return e;
   GemmArgs d = g;
@@ -367,7 +369,7 @@ hipError_t launch_combine(const moe_config_t& c, const void* y_perm, const int32
   d.out_f32 = 1;
   {
     ProfScope p(MOE_K_SHARED_DOWN_COMBINE, st);
-    e = lds ? launch_lds_down(false, ms, mt, d, st) : launch_rs_down(MOE_RECIPE_BF16, ms, mt, d, st, 1);
+    e = launch_lds_down(false, mt, d, st);
   }
   if (e != hipSuccess) return e;
   ProfScope p(MOE_K_COMBINE, st);
@@ -409,18 +411,18 @@ static hipError_t forward_impl(const moe_config_t& c, const void* x, const void*
   float* w = topk_w_out ? topk_w_out : at<float>(ws, L.w);
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* pos = at<int32_t>(ws, L.pos);
-  void* x_perm = at<void>(ws, L.x_perm);
-  void* x_perm_scale = act_scaled(c) ? at<void>(ws, L.x_perm_scale) : nullptr;
+  void* xq = at<void>(ws, L.xq);
+  void* xq_scale = act_scaled(c) ? at<void>(ws, L.xq_scale) : nullptr;
   void* y_perm = at<void>(ws, L.y_perm);
   int32_t* sorted = at<int32_t>(ws, L.sorted);
   hipError_t e = launch_route(c, x, gate_w, bias, idx, w, at<float>(ws, L.logits), at<double>(ws, L.gate_partial), st);
   // Fused gather: the routed GEMMs read the token rows of x (or of its quantised
   // copy, made once per token) through the sorted pair order, with no gathered copy.
   if (e == hipSuccess) e = launch_permute(c, idx, x, offsets, sorted, pos, nullptr, nullptr, at<int32_t>(ws, L.hist), st);
-  if (e == hipSuccess && quantised(c)) e = launch_quantize_tokens(c, x, x_perm, x_perm_scale, st);
+  if (e == hipSuccess && quantised(c)) e = launch_quantize_tokens(c, x, xq, xq_scale, st);
   if (e == hipSuccess) {
     FfnScratch sc{at<int32_t>(ws, L.tiles_l), at<int32_t>(ws, L.tiles_s), at<void>(ws, L.h), at<void>(ws, L.h_scale)};
-    e = launch_grouped_ffn(c, offsets, quantised(c) ? x_perm : x, x_perm_scale, sorted, *experts, y_perm, sc, st);
+    e = launch_grouped_ffn(c, offsets, quantised(c) ? xq : x, xq_scale, sorted, *experts, y_perm, sc, st);
   }
   if (e == hipSuccess)
     e = launch_combine(c, y_perm, pos, w, x, shared, resid, out, at<void>(ws, L.h_shared), at<float>(ws, L.sh_out),
@@ -576,6 +578,20 @@ moe_status_t moe_forward_residual(const moe_config_t* cfg, const void* resid, co
   if (e == hipSuccess)
     e = forward_impl(*cfg, xn, resid, gate_w, bias, experts, shared, out, topk_idx_out, topk_w_out, ws, st);
   return to_status(e);
+}
+
+moe_status_t moe_convert_mxfp4_to_fp8(int64_t rows, int32_t row_len, const void* w_fp4, const void* w_e8m0,
+                                      void* w_fp8, float* w_fp8_scale, int32_t* inexact_blocks, void* stream) {
+  if (rows < 0 || row_len <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (rows % 128 != 0 || row_len % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!w_fp4 || !w_e8m0 || !w_fp8 || !w_fp8_scale) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(w_fp4) || !aligned16(w_fp8) || !aligned16(w_fp8_scale) ||
+      (reinterpret_cast<uintptr_t>(w_e8m0) & 15) || (reinterpret_cast<uintptr_t>(inexact_blocks) & 3))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (rows / 128 > 65535) return MOE_ERR_UNSUPPORTED;
+  return to_status(launch_mxfp4_to_fp8(rows, row_len, w_fp4, w_e8m0, w_fp8, w_fp8_scale, inexact_blocks,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_pack_fp4_scales(int32_t recipe, int64_t rows, int32_t row_len, const void* src, void* dst,

@@ -66,6 +66,10 @@ reason in the design notes):
            saturating at 6 and keeping the sign bit;
      the value is q * s.  No per-tensor scale (the page names none).  The
      activations are the rows fed to the routed experts (x and h), as in R7.
+  R14 FP4 -> FP8 conversion (V4-Pro overview, convert.py: lossless e2m1fn to
+     e4m3fn with care for the scales): MXFP4 weights become e4m3fn codes with one
+     fp32 scale per 128 x 128 block, 2^(largest E8M0 exponent of the block's
+     groups); see convert_mxfp4_to_fp8.
 """
 from __future__ import annotations
 
@@ -483,3 +487,28 @@ def gather_rows(recipe: int, x32: np.ndarray, sorted_pair: np.ndarray, k: int):
 def mxfp4_bytes_per_param() -> float:
     """Storage of one MXFP4 parameter: a 4-bit element plus one 8-bit scale per 32."""
     return 0.5 + 1.0 / 32.0
+
+
+# =============================================================== FP4 -> FP8 weight conversion
+def convert_mxfp4_to_fp8(q_packed: np.ndarray, e8m0: np.ndarray):
+    """MXFP4 weights -> the fp8 recipe's format (e4m3fn codes, one fp32 scale per
+    128 x 128 block): the DeepSeek-V4-Pro overview's convert.py entry converts FP4
+    (e2m1fn) to FP8 (e4m3fn) losslessly, with care for the scales.
+
+    Reading (R14): the scale of block B is 2^(E_B - 127) with E_B the largest E8M0
+    byte of the per-32 groups in B; an element of a group with byte b and e2m1 value q
+    becomes e4m3(q * 2^(b - E_B)), rounding to nearest, ties to the even code.  Every
+    e2m1 value is an e4m3 value, so the block is reproduced exactly whenever its
+    groups' exponents differ by at most 8 (0.5 * 2^-8 is e4m3's smallest subnormal).
+    q_packed [R, K/2] (low nibble = even k), e8m0 [R, K/32]; R, K multiples of 128.
+    Returns (codes uint8 [R, K], scales fp32 [R/128, K/128], blocks not reproduced)."""
+    v = decode_e2m1_packed(q_packed)
+    R, K = v.shape
+    b = e8m0.astype(np.int64)
+    E = b.reshape(R // 128, 128, K // 128, 4).max(axis=(1, 3))
+    d = np.repeat(np.repeat(E, 128, axis=0), 128, axis=1) - np.repeat(b, 32, axis=1)
+    x = v * np.ldexp(1.0, -d)                           # exact in fp64
+    codes = encode_e4m3(x)
+    scales = np.ldexp(1.0, E - 127).astype(F32)
+    exact = (decode_e4m3(codes) == x).reshape(R // 128, 128, K // 128, 128).all(axis=(1, 3))
+    return codes, scales, int((~exact).sum())

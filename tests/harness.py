@@ -91,7 +91,76 @@ def oracle(inp: G.MoEInputs, tokens=None):
 
 
 def sample_tokens(T: int, n: int, seed: int = 0) -> np.ndarray:
-    """First, last and random tokens (sorted, unique)."""
+    """Token 0, token T-1 and n-2 other random tokens (sorted, unique; all tokens when n >= T)."""
+    if n >= T:
+        return np.arange(T)
     rng = np.random.default_rng(seed)
-    pick = set([0, T - 1]) | set(rng.choice(T, size=min(n, T), replace=False).tolist())
-    return np.array(sorted(pick)[:max(n, 2)])
+    rest = rng.choice(np.arange(1, T - 1), size=max(0, min(n - 2, T - 2)), replace=False) if T > 2 else []
+    return np.array(sorted(set([0, T - 1]) | set(np.asarray(rest).tolist())))
+
+
+def cover_tokens(idx: np.ndarray, offsets: np.ndarray, sorted_pair: np.ndarray, n_largest: int = 3,
+                 tile: int = 256) -> np.ndarray:
+    """Tokens whose outputs exercise every expert and every row tile of the largest experts.
+
+    Greedy: tokens are added until every expert with rows has at least one of its
+    (token, slot) pairs among them; then, for each of the n_largest experts, the
+    tokens of the first and last row of every `tile`-row block of its rows (the GEMM
+    row tiles, including the ragged last one); plus the first and last token."""
+    T, k = idx.shape
+    E = len(offsets) - 1
+    need = set(np.nonzero(np.diff(offsets) > 0)[0].tolist())
+    chosen = {0, T - 1}
+    for t in (0, T - 1):
+        need -= set(idx[t].tolist())
+    for t in range(T):
+        if not need:
+            break
+        new = need & set(idx[t].tolist())
+        if new:
+            chosen.add(t)
+            need -= new
+    counts = np.diff(offsets)
+    for e in np.argsort(-counts, kind="stable")[:n_largest]:
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        for r0 in range(lo, hi, tile):
+            for r in (r0, min(r0 + tile, hi) - 1):
+                chosen.add(int(sorted_pair[r]) // k)
+    return np.array(sorted(chosen))
+
+
+def oracle_tokens(inp: G.MoEInputs, tokens: np.ndarray, routing, perm, workers: int = 16):
+    """The oracle's outputs for `tokens` (routing and permutation given), computed over
+    `workers` groups of tokens in a thread pool with one BLAS thread each; returns out
+    [len(tokens), H] in the order of `tokens`.  Tokens are grouped so that each group
+    touches few experts beyond the others' (the oracle dequantises every expert a
+    group touches)."""
+    import concurrent.futures as cf
+    from threadpoolctl import threadpool_limits
+    cfg = inp.cfg
+    x = x_f64(inp)
+    gw, b = inp.gate_w.double().cpu().numpy(), inp.bias.cpu().numpy()
+    s13, s2 = shared_f64(inp)
+    raw = expert_raw_fn(inp)
+    idx = routing["idx"]
+    nb = max(1, min(workers, len(tokens)))
+    bins, sets = [[] for _ in range(nb)], [set() for _ in range(nb)]
+    cap = -(-len(tokens) // nb)
+    for t in tokens:                                    # greedy: fewest new experts, then emptiest group
+        ex = set(idx[t].tolist())
+        best = min((i for i in range(nb) if len(bins[i]) < cap), key=lambda i: (len(ex - sets[i]), len(sets[i])))
+        bins[best].append(int(t))
+        sets[best] |= ex
+
+    def run(tk):
+        return O.moe_forward(cfg, x, gw, b, raw, s13, s2, tokens=np.array(tk), routing=routing, perm=perm)["out"]
+
+    with threadpool_limits(1), cf.ThreadPoolExecutor(max_workers=nb) as ex:
+        outs = list(ex.map(run, [bn for bn in bins if bn]))
+    got = dict(zip([t for bn in bins if bn for t in bn], np.concatenate(outs, axis=0)))
+    return np.stack([got[int(t)] for t in tokens])
+
+
+def row_rel_l2(got: np.ndarray, want: np.ndarray) -> np.ndarray:
+    """Relative L2 error of each row."""
+    return np.linalg.norm(got - want, axis=1) / np.maximum(np.linalg.norm(want, axis=1), 1e-300)

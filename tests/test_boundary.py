@@ -122,3 +122,21 @@ def test_pack_fp4_scales_argument_checks(recipe, rows, row_len, src, dst, want):
     lib = M.load()
     p = lambda a: None if a is None else ctypes.c_void_p(a)
     assert lib.moe_pack_fp4_scales(recipe, rows, row_len, p(src), p(dst), None) == want
+
+
+@pytest.mark.parametrize("rows,row_len,ptrs,want", [
+    (-128, 256, (1 << 20, 1 << 21, 1 << 22, 1 << 23, None), 1),
+    (128, 0, (1 << 20, 1 << 21, 1 << 22, 1 << 23, None), 1),
+    (96, 256, (1 << 20, 1 << 21, 1 << 22, 1 << 23, None), 2),     # rows not a multiple of 128
+    (128, 192, (1 << 20, 1 << 21, 1 << 22, 1 << 23, None), 2),    # row length not a multiple of 128
+    (128, 256, (None, 1 << 21, 1 << 22, 1 << 23, None), 1),
+    (128, 256, (1 << 20, 1 << 21, None, 1 << 23, None), 1),
+    (128, 256, (1 << 20, (1 << 21) + 2, 1 << 22, 1 << 23, None), 1),   # misaligned scales
+    (128, 256, (1 << 20, 1 << 21, 1 << 22, 1 << 23, (1 << 24) + 2), 1),   # misaligned counter
+    (0, 256, (None, None, None, None, None), 0),                    # no rows: a no-op
+])
+def test_convert_mxfp4_to_fp8_argument_checks(rows, row_len, ptrs, want):
+    """Rejected before anything is enqueued (the pointers are never dereferenced)."""
+    lib = M.load()
+    p = lambda a: None if a is None else ctypes.c_void_p(a)
+    assert lib.moe_convert_mxfp4_to_fp8(rows, row_len, *[p(a) for a in ptrs], None) == want

@@ -538,3 +538,214 @@ def test_quantised_recipes_quantise_the_expert_inputs(recipe):
     assert np.abs(xq - x).max() > 0                                   # the quantisation is not a no-op
     r2 = O.moe_forward(cfg, xq, gw, b, HN.expert_raw_fn(inp), s13, s2, tokens=tokens, routing=r1["routing"])
     np.testing.assert_array_equal(r1["y"], r2["y"])
+
+
+# ------------------------------------------------------------------ selection key (R3)
+def test_selection_key_is_the_fp32_sum_and_fp32_ties_go_to_the_lower_index():
+    """The walk-through (section 3.2) adds e_score_correction_bias to each score;
+    R3 takes that sum in fp32.  Two experts whose exact sums differ by 2^-30 tie in
+    fp32 (half an ulp near 0.7 is 3e-8), so the lower index must win; a key kept in
+    fp64 would pick the higher one."""
+    s = np.array([[0.6, 0.7, 0.7, 0.1, 0.3]], dtype=F32)
+    b = np.array([0.0, 0.0, 2.0 ** -30, -0.1, 0.25], dtype=F32)
+    key = O.selection_key(s, b)
+    for e in range(5):
+        assert key[0, e] == fp32_nearest(Fraction(float(s[0, e])) + Fraction(float(b[e])))
+    assert key[0, 1] == key[0, 2]
+    # the same tie through the router: experts 1 and 2 have the same gate row
+    cfg = rand_small_cfg(num_tokens=16, hidden=32, num_experts=8, top_k=1)
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((16, 32)).astype(F32).astype(np.float64)
+    gw = (rng.standard_normal((8, 32)) * 0.01).astype(F32).astype(np.float64)
+    gw[1] = gw[2] = 0.05                            # equal rows that dominate for positive x
+    x = np.abs(x)
+    bias = np.zeros(8, dtype=F32)
+    bias[2] = F32(2.0 ** -30)
+    r = O.route(cfg, x, gw, bias)
+    assert np.all(r["key"][:, 1] == r["key"][:, 2])
+    assert np.all(r["idx"][:, 0] == 1)
+
+
+# ------------------------------------------------------------------ quantised expert path (R7, R13)
+def _e4m3_value(v: float) -> float:
+    """e4m3fn rounding of an fp32 value by torch's cast, saturating at 448 (R7)."""
+    v = max(-448.0, min(448.0, v))
+    return float(torch.tensor(v, dtype=torch.float32).to(torch.float8_e4m3fn).to(torch.float64))
+
+
+_E2M1_GRID = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _e2m1_value(v: float) -> float:
+    """Nearest e2m1 grid value, ties to the even code, saturating at 6 (sign kept)."""
+    a = min(abs(v), 6.0)
+    best = min(range(8), key=lambda c: (abs(_E2M1_GRID[c] - a), c % 2))
+    return math.copysign(_E2M1_GRID[best], v)
+
+
+def _quant_row_loops(recipe: int, row32) -> list:
+    """One fp32 row quantised and dequantised block by block, written from R7 / R13."""
+    out = []
+    if recipe == O.RECIPE_FP8_B128:
+        for b0 in range(0, len(row32), 128):
+            blk = [float(v) for v in row32[b0:b0 + 128]]
+            amax = max(abs(v) for v in blk)
+            s = float(F32(amax) / F32(448.0)) if amax > 0 else 1.0
+            out += [_e4m3_value(float(F32(v) / F32(s))) * s for v in blk]
+    elif recipe == O.RECIPE_MXFP4:                     # MXFP8 activations
+        for b0 in range(0, len(row32), 32):
+            blk = [float(v) for v in row32[b0:b0 + 32]]
+            amax = max(abs(v) for v in blk)
+            e = 0
+            if amax > 0:
+                e = -200
+                while amax > 448.0 * 2.0 ** e:
+                    e += 1
+            e = max(-127, min(127, e))
+            out += [_e4m3_value(v * 2.0 ** -e) * 2.0 ** e for v in blk]
+    elif recipe == O.RECIPE_NVFP4:
+        for b0 in range(0, len(row32), 16):
+            blk = [float(v) for v in row32[b0:b0 + 16]]
+            amax = max(abs(v) for v in blk)
+            s = _e4m3_value(float(F32(amax) / F32(6.0)))
+            s = s if s > 0 else 1.0
+            out += [_e2m1_value(float(F32(v) / F32(s))) * s for v in blk]
+    else:
+        raise ValueError(recipe)
+    return out
+
+
+def _mlp_loops(xrow, w13, w2, quant_recipe=None):
+    """SwiGLU MLP of one row with math.fsum dot products; h quantised per recipe."""
+    I = w13.shape[0] // 2
+    g = [math.fsum(w13[i, k] * xrow[k] for k in range(len(xrow))) for i in range(I)]
+    u = [math.fsum(w13[I + i, k] * xrow[k] for k in range(len(xrow))) for i in range(I)]
+    h = [gi / (1.0 + math.exp(-gi)) * ui for gi, ui in zip(g, u)]
+    if quant_recipe is not None:
+        h = _quant_row_loops(quant_recipe, np.array(h).astype(F32))
+    return [math.fsum(w2[o, i] * h[i] for i in range(I)) for o in range(w2.shape[0])]
+
+
+@pytest.mark.parametrize("recipe", [O.RECIPE_FP8_B128, O.RECIPE_MXFP4, O.RECIPE_NVFP4])
+def test_quantised_layer_matches_scalar_loops(recipe):
+    """A tiny quantised layer against loops written from R7 / R13: the routed
+    experts see x and h quantised per (row, 128) fp8 / (row, 32) MXFP8 / (row, 16)
+    NVFP4 blocks, while the shared expert sees the unquantised x (walk-through
+    section 4: shared experts stay high precision).  A wrong block size, a missed
+    h quantisation or a quantised shared input all move the result by about 1e-2."""
+    base = {O.RECIPE_FP8_B128: C.MINI_FP8, O.RECIPE_MXFP4: C.MINI_MXFP4, O.RECIPE_NVFP4: C.MINI_NVFP4}[recipe]
+    cfg = base.replace(name="pin_" + base.name, num_tokens=3, hidden=256, intermediate=128, num_experts=4,
+                       top_k=2, num_shared=1, shared_intermediate=128, n_group=1, topk_group=1)
+    inp = G.generate(cfg)
+    from tests import harness as HN
+    x = HN.x_f64(inp)
+    gw, b = inp.gate_w.double().numpy(), inp.bias.numpy()
+    s13, s2 = HN.shared_f64(inp)
+    raw = HN.expert_raw_fn(inp)
+    got = O.moe_forward(cfg, x, gw, b, raw, s13, s2)
+    idx, w = got["routing"]["idx"], got["routing"]["w"].astype(np.float64)
+    for t in range(cfg.num_tokens):
+        xq = _quant_row_loops(recipe, x[t].astype(F32))
+        want = np.zeros(cfg.hidden)
+        for j in range(cfg.top_k):
+            w13, w2 = O.dequant_expert(recipe, raw(int(idx[t, j])), cfg.intermediate, cfg.hidden)
+            want += w[t, j] * np.array(_mlp_loops(xq, w13, w2, quant_recipe=recipe))
+        want += np.array(_mlp_loops(list(x[t]), s13[0], s2[0]))
+        np.testing.assert_allclose(got["out"][t], want, rtol=1e-9, atol=1e-12)
+
+
+def test_nvfp4_weight_dequantisation_against_the_source_weights():
+    """NVFP4 (walk-through section 4: 4-bit weights, one FP8 scale per 16): the
+    dequantised weights lie within half an e2m1 step (times the group scale) of the
+    fp32 source values, except where the group's largest value saturates at 6 x
+    scale; each scale is the e4m3 value nearest to amax / 6."""
+    g = torch.Generator().manual_seed(3)
+    w = torch.randn(64, 256, generator=g) * 0.02
+    w[5, 16:32] = 0.0
+    q, sc = G.encode_nvfp4(w)
+    d = O.dequant_expert(C.RECIPE_NVFP4, {"w13": q.numpy(), "w13_scale": sc.numpy(),
+                                         "w2": q.numpy(), "w2_scale": sc.numpy()}, 32, 256)[0]
+    ref = w.double().numpy()
+    s = np.array([[_e4m3_value(float(F32(a) / F32(6.0))) or 1.0 for a in row]
+                  for row in np.abs(ref).reshape(64, 16, 16).max(axis=2)])
+    np.testing.assert_array_equal(O.decode_e4m3(sc.numpy()), s)
+    sfull = np.repeat(s, 16, axis=1)
+    a = np.abs(ref) / sfull
+    step = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
+    bound = 0.5 * step * sfull + np.maximum(0.0, np.abs(ref) - 6.0 * sfull)
+    assert np.all(np.abs(d - ref) <= bound + 1e-30)
+    assert np.all(d[5, 16:32] == 0.0)
+
+
+def test_residual_form_matches_scalar_loops():
+    """Decoder-layer residual form (walk-through section 3.5): out = h + MoE(x) with
+    x = RMSNorm(h) per row, (h * r) * weight, r = 1 / sqrt(mean(h^2) + eps), rounded
+    to fp32 and then to bf16 (R12).  The norm is written here with math.fsum and
+    torch's bf16 cast; the MoE part is the oracle's own (pinned above)."""
+    cfg = C.MINI_GROUPED_BF16.replace(name="pin_resid", num_tokens=5)
+    inp = G.generate(cfg)
+    from tests import harness as HN
+    h = HN.x_f64(inp)
+    nw = (1.0 + 0.1 * np.random.default_rng(4).standard_normal(cfg.hidden)).astype(F32)
+    eps = 1e-6
+    x = np.empty_like(h)
+    for t in range(cfg.num_tokens):
+        r = 1.0 / math.sqrt(math.fsum(v * v for v in h[t]) / cfg.hidden + eps)
+        y32 = torch.tensor([(v * r) * float(wv) for v, wv in zip(h[t], nw)], dtype=torch.float64).to(torch.float32)
+        x[t] = y32.to(torch.bfloat16).to(torch.float64).numpy()
+    gw, b = inp.gate_w.double().numpy(), inp.bias.numpy()
+    s13, s2 = HN.shared_f64(inp)
+    got = O.moe_forward_residual(cfg, h, nw, eps, gw, b, HN.expert_raw_fn(inp), s13, s2)
+    np.testing.assert_array_equal(got["x"], x)
+    plain = O.moe_forward(cfg, x, gw, b, HN.expert_raw_fn(inp), s13, s2)
+    np.testing.assert_array_equal(got["out"], h + plain["out"])
+    # token subset: rows line up with their residual rows
+    sub = O.moe_forward_residual(cfg, h, nw, eps, gw, b, HN.expert_raw_fn(inp), s13, s2, tokens=np.array([4, 1]))
+    np.testing.assert_allclose(sub["out"], got["out"][[4, 1]], rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------ FP4 -> FP8 conversion (R14)
+def _mx_block(rng, rows=128, cols=256, spread=3):
+    """Random MXFP4 weights whose per-32 exponents (E8M0 bytes) span `spread` + 1 values."""
+    codes = rng.integers(0, 16, (rows, cols), dtype=np.uint8)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    e8 = (120 + rng.integers(0, spread + 1, (rows, cols // 32))).astype(np.uint8)
+    return packed, e8
+
+
+def test_mxfp4_to_fp8_is_lossless_within_an_exponent_spread_of_8():
+    """V4-Pro overview, convert.py: the FP4 -> FP8 conversion is lossless.  With the
+    groups of every 128 x 128 block within 8 binades, each converted value times its
+    block scale equals the MXFP4 value exactly (MX dequantisation, pinned above)."""
+    rng = np.random.default_rng(11)
+    packed, e8 = _mx_block(rng, 256, 384, spread=8)
+    codes, scales, bad = O.convert_mxfp4_to_fp8(packed, e8)
+    assert bad == 0
+    want = O.dequant_expert(C.RECIPE_MXFP4, {"w13": packed, "w13_scale": e8, "w2": packed, "w2_scale": e8}, 128, 384)[0]
+    got = O.decode_e4m3(codes) * np.repeat(np.repeat(scales.astype(np.float64), 128, 0), 128, 1)
+    np.testing.assert_array_equal(got, want)
+    # the fp8 recipe's own dequantisation reads the converted weights as the same values
+    fp8 = O.dequant_expert(C.RECIPE_FP8_B128, {"w13": codes, "w13_scale": scales, "w2": codes, "w2_scale": scales},
+                           128, 384)[0]
+    np.testing.assert_array_equal(fp8, want)
+
+
+def test_mxfp4_to_fp8_rounds_and_counts_blocks_beyond_the_spread():
+    """A block whose groups span more than 8 binades cannot keep its smallest values:
+    they round to the nearest e4m3 value (ties to even, checked against an exact
+    brute-force search with fractions) and the block is counted."""
+    rng = np.random.default_rng(12)
+    packed, e8 = _mx_block(rng, 128, 256, spread=2)
+    e8[5, 1] = 110                                   # 10 and more binades below the block maximum
+    e8[9, 6] = 100
+    codes, scales, bad = O.convert_mxfp4_to_fp8(packed, e8)
+    assert bad >= 1
+    pos = [Fraction(float(v)) for v in O.E4M3_TABLE[:0x7F]]
+    v = O.decode_e2m1_packed(packed)
+    for r, g in ((5, 1), (9, 6)):
+        E = int(e8[(r // 128) * 128:(r // 128 + 1) * 128, (g // 4) * 4:(g // 4 + 1) * 4].max())
+        for c in range(32 * g, 32 * g + 32):
+            x = Fraction(float(v[r, c])) * Fraction(2) ** (int(e8[r, g]) - E)
+            ranked = sorted(range(len(pos)), key=lambda i: (abs(pos[i] - abs(x)), i % 2))
+            want = float(pos[ranked[0]]) * (-1.0 if math.copysign(1.0, float(v[r, c])) < 0 else 1.0)
+            assert O.decode_e4m3(codes[r:r + 1, c:c + 1])[0, 0] == want
