@@ -214,6 +214,29 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* ga
                          const moe_weights_t* shared, void* out, int32_t* topk_idx_out,
                          float* topk_w_out, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation and kernels as moe_forward, with the scratch taken from a static
+ * device array the library holds on each GPU it runs on (from the first call on
+ * that GPU until the process ends) instead of a caller workspace.  The caller still
+ * passes inputs and outputs, as for moe_forward.
+ *   - Configurations whose moe_workspace_bytes exceeds
+ *     moe_forward_noalloc_scratch_bytes() (128 MiB: the decode shapes, e.g.
+ *     T = 128, H = 7168, 384 experts, top-8, I = 2048 needs 68 MiB) return
+ *     MOE_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.
+ *   - Every call on one GPU uses that GPU's one array: calls that can overlap on a
+ *     GPU (other streams, other threads) race and must be serialised by the
+ *     caller.  The array keeps the last call's contents; no call relies on it
+ *     starting at zero.
+ *   - MOE_ERR_LAUNCH also reports a failed lookup of the array's device address. */
+moe_status_t moe_forward_noalloc(const moe_config_t* cfg, const void* x, const float* gate_w,
+                                 const float* bias, const moe_weights_t* experts,
+                                 const moe_weights_t* shared, void* out, int32_t* topk_idx_out,
+                                 float* topk_w_out, void* stream);
+
+/* Bytes of moe_forward_noalloc's static scratch array (its size limit). */
+size_t moe_forward_noalloc_scratch_bytes(void);
+
 /* post_attention_layernorm (walk-through section 3.5; RMSNorm kept in fp32 in
  * the V4-Pro overview): for each token row t of the residual stream resid [T][H]
  * (fp32 for F32, else bf16),

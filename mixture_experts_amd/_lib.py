@@ -17,7 +17,8 @@ RECIPE_F32, RECIPE_BF16, RECIPE_FP8_B128, RECIPE_MXFP4, RECIPE_NVFP4 = range(5)
 SCORE_SIGMOID, SCORE_SQRTSOFTPLUS = range(2)
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
-           "moe_forward", "moe_rmsnorm", "moe_forward_residual", "moe_pack_fp4_scales", "moe_convert_mxfp4_to_fp8",
+           "moe_forward", "moe_forward_noalloc", "moe_forward_noalloc_scratch_bytes", "moe_rmsnorm",
+           "moe_forward_residual", "moe_pack_fp4_scales", "moe_convert_mxfp4_to_fp8",
            "moe_status_string", "moe_profile_start", "moe_profile_stop", "moe_kernel_tag_name")
 KERNEL_TAGS = ("gate_logits", "router", "perm_hist", "perm_scan", "perm_scatter", "gather", "tile_list",
                "ffn_gate_up", "ffn_down", "shared_gate_up", "shared_down_combine", "combine", "rmsnorm")
@@ -71,6 +72,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.moe_grouped_ffn.argtypes = [cfgp, vp, vp, vp, wp, vp, vp, sz, vp]
     lib.moe_combine.argtypes = [cfgp, vp, vp, vp, vp, wp, vp, vp, sz, vp]
     lib.moe_forward.argtypes = [cfgp, vp, vp, vp, wp, wp, vp, vp, vp, vp, sz, vp]
+    lib.moe_forward_noalloc.argtypes = [cfgp, vp, vp, vp, wp, wp, vp, vp, vp, vp]
+    lib.moe_forward_noalloc_scratch_bytes.argtypes = []
+    lib.moe_forward_noalloc_scratch_bytes.restype = sz
     lib.moe_rmsnorm.argtypes = [cfgp, vp, vp, ctypes.c_float, vp, vp]
     lib.moe_forward_residual.argtypes = [cfgp, vp, vp, ctypes.c_float, vp, vp, wp, wp, vp, vp, vp, vp, sz, vp]
     lib.moe_pack_fp4_scales.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
@@ -79,7 +83,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.moe_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), ctypes.c_int32]
     lib.moe_kernel_tag_name.argtypes = [ctypes.c_int32]
     lib.moe_kernel_tag_name.restype = ctypes.c_char_p
-    for name in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_rmsnorm",
+    for name in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_forward_noalloc",
+                 "moe_rmsnorm",
                  "moe_forward_residual", "moe_pack_fp4_scales", "moe_convert_mxfp4_to_fp8", "moe_profile_start",
                  "moe_profile_stop"):
         getattr(lib, name).restype = i32
@@ -198,6 +203,18 @@ def moe_forward(cfg, x, gate_w, bias, experts: MoeWeights, shared: MoeWeights | 
                               ctypes.byref(shared) if shared is not None else None, _ptr(out), _ptr(topk_idx_out),
                               _ptr(topk_w_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "moe_forward")
+
+
+def moe_forward_noalloc(cfg, x, gate_w, bias, experts: MoeWeights, shared: MoeWeights | None, out, topk_idx_out,
+                        topk_w_out, stream=None):
+    """moe_forward with the library's static scratch instead of a workspace (include/moe.h)."""
+    _check(load().moe_forward_noalloc(ctypes.byref(cfg), _ptr(x), _ptr(gate_w), _ptr(bias), ctypes.byref(experts),
+                                      ctypes.byref(shared) if shared is not None else None, _ptr(out),
+                                      _ptr(topk_idx_out), _ptr(topk_w_out), _stream(stream)), "moe_forward_noalloc")
+
+
+def moe_forward_noalloc_scratch_bytes() -> int:
+    return int(load().moe_forward_noalloc_scratch_bytes())
 
 
 def moe_rmsnorm(cfg, resid, norm_w, eps: float, x, stream=None):

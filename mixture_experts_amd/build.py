@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
 FLAT_LIB = os.path.join(PKG, "libmoe_mi355x_flatcopy.so")
 SOURCES = ["moe_api.hip", "route.hip", "permute.hip", "ffn_rs.hip", "ffn_misc.hip", "ffn_lds.hip", "norm.hip",
-           "convert.hip"]
+           "convert.hip", "noalloc.hip"]
 FLAT_SOURCES = ["ffn_rs.hip", "ffn_lds.hip"]          # the files MOE_FORCE_FLAT_COPIES changes
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
