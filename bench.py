@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--config", default="decode_bf16")
     ap.add_argument("--extra-configs", default=",".join(EXTRA_CONFIGS),
                     help="comma-separated workloads also measured in this run ('' for none)")
-    ap.add_argument("--cpu-experts", type=int, default=32, help="experts in the oracle's timed FFN sample")
+    ap.add_argument("--cpu-budget", type=float, default=30.0,
+                    help="seconds of single-core oracle FFN time before the rest is scaled from the experts done")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--residual", action="store_true",
                     help="time the residual form instead: out = h + MoE(RMSNorm(h)) (moe_forward_residual)")
@@ -197,14 +198,15 @@ def fractions(cfg, counts, prof, steps):
     return touched, gu, rt
 
 
-def cpu_baseline(cfg, inp, n_experts):
-    """The oracle (numpy fp64, as it stands) on the whole workload's token set, timed on
-    the host.  Routing and permutation of all T tokens and the shared expert(s) over
-    all T tokens are timed in full.  The routed FFN -- per touched expert: dequantise
-    its weights, run its MLP on all of its rows -- is timed on a sample of n_experts
-    touched experts and scaled to all of them.  Primary figure: one core (BLAS and
-    every step on one thread).  Secondary: all host cores, the sampled experts spread
-    over a thread pool (one BLAS thread each)."""
+def cpu_baseline(cfg, inp, budget_s):
+    """The oracle (numpy fp64, as it stands) on the whole workload, timed on the host.
+    Routing and permutation of all T tokens and the shared expert(s) over all T tokens
+    are timed in full.  The routed FFN -- per touched expert: dequantise its weights,
+    run its MLP on all of its rows -- is timed expert by expert in a seeded random
+    order until every touched expert is done or budget_s has passed; in the second
+    case the time is scaled to all touched experts (the sample says which).
+    Primary figure: one core (BLAS and every step on one thread).  Secondary: all
+    host cores (up to 16 threads, one BLAS thread each, over all touched experts)."""
     import concurrent.futures as cf
 
     import numpy as np
@@ -212,7 +214,7 @@ def cpu_baseline(cfg, inp, n_experts):
 
     from oracle import moe_oracle as O
     from tests import harness as HN
-    T, k, I, H = cfg.num_tokens, cfg.top_k, cfg.intermediate, cfg.hidden
+    T, I, H = cfg.num_tokens, cfg.intermediate, cfg.hidden
     quant = cfg.recipe in (O.RECIPE_FP8_B128, O.RECIPE_MXFP4, O.RECIPE_NVFP4)
     # host copies of the inputs (not timed: I/O, not oracle work)
     x64 = HN.x_f64(inp)
@@ -226,9 +228,8 @@ def cpu_baseline(cfg, inp, n_experts):
         O.permute(routing["idx"], cfg.num_experts)
         t_route = time.perf_counter() - t0
     idx = routing["idx"]
-    touched = np.unique(idx)
-    sample = np.random.default_rng(1).choice(touched, size=min(n_experts, touched.size), replace=False)
-    raw = {int(e): raw_fn(int(e)) for e in sample}
+    touched = np.random.default_rng(1).permutation(np.unique(idx))
+    raw = {int(e): raw_fn(int(e)) for e in touched}
     xq = O.quantize_rows(cfg.recipe, x64.astype(np.float32)) if quant else x64
 
     def one_expert(e):                                   # moe_forward's per-expert step
@@ -237,39 +238,43 @@ def cpu_baseline(cfg, inp, n_experts):
         return O.expert_mlp(xq[rows], w13, w2, cfg.recipe, quantize_h=quant)
 
     with threadpool_limits(1):
-        t0 = time.perf_counter()
-        for e in sample:
+        done, t0 = 0, time.perf_counter()
+        for e in touched:
             one_expert(e)
-        t_sample = time.perf_counter() - t0
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        t_ffn = time.perf_counter() - t0
         t0 = time.perf_counter()
         for s in range(s13.shape[0]):
             O.expert_mlp(x64, s13[s], s2[s])
         t_shared = time.perf_counter() - t0
-    t1 = t_route + t_shared + t_sample / len(sample) * touched.size
+    t1 = t_route + t_shared + t_ffn / done * touched.size
     ncpu = os.cpu_count() or 1
     workers = min(ncpu, 16)
     with threadpool_limits(1), cf.ThreadPoolExecutor(max_workers=workers) as ex:
         t0 = time.perf_counter()
-        list(ex.map(one_expert, sample))
-        t_sample_mt = time.perf_counter() - t0
+        list(ex.map(one_expert, touched))
+        t_ffn_mt = time.perf_counter() - t0
     with threadpool_limits(workers):
         t0 = time.perf_counter()
         for s in range(s13.shape[0]):
             O.expert_mlp(x64, s13[s], s2[s])
         t_shared_mt = time.perf_counter() - t0
-    tn = t_route + t_shared_mt + t_sample_mt / len(sample) * touched.size
+    tn = t_route + t_shared_mt + t_ffn_mt
     model = platform.processor() or ""
     try:
         with open("/proc/cpuinfo") as f:
             model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), model)
     except OSError:
         pass
+    ffn = (f"the routed FFN of all {touched.size} touched experts ({t_ffn:.1f} s)" if done == touched.size else
+           f"the routed FFN timed on {done} of the {touched.size} touched experts (all their rows; {t_ffn:.1f} s) "
+           f"and scaled to all of them")
     return {"value": round(T / t1, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"all {T} tokens: routing + permutation and the shared expert timed in full "
-                      f"({t_route + t_shared:.1f} s); routed FFN timed on {len(sample)} of the {touched.size} "
-                      f"touched experts (all their rows; {t_sample:.1f} s) and scaled to all of them; "
-                      f"estimated whole-workload time {t1:.1f} s on one core",
-            "all_cores": {"value": round(T / tn, 4), "threads": workers, "estimated_s": round(tn, 2)},
+            "sample": f"the whole workload, all {T} tokens, on one core: routing + permutation and the shared "
+                      f"expert ({t_route + t_shared:.1f} s), {ffn}; {t1:.1f} s in all",
+            "all_cores": {"value": round(T / tn, 4), "threads": workers, "seconds": round(tn, 2)},
             "nproc": ncpu, "cpu_model": model}
 
 
@@ -327,7 +332,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
-        line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_experts)
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)
         print(f"[bench] cpu baseline in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
         if args.residual:
             line["cpu_baseline"]["sample"] += " (MoE part of the residual form)"
