@@ -22,9 +22,10 @@ struct ProfScope {
   ~ProfScope() { prof_end(tag, st); }
 };
 
-int gate_ksplit(const moe_config_t& c);   // K splits of the gate GEMM (1 = none)
+// Route scratch (gate logits or screened partial sums, split gate weights, norms).
+size_t route_workspace_bytes(const moe_config_t& c);
 hipError_t launch_route(const moe_config_t& c, const void* x, const float* gate_w, const float* bias,
-                        int32_t* topk_idx, float* topk_w, float* logits_ws, double* partial_ws, hipStream_t st);
+                        int32_t* topk_idx, float* topk_w, void* route_ws, hipStream_t st);
 
 hipError_t launch_permute(const moe_config_t& c, const int32_t* topk_idx, const void* x, int32_t* offsets,
                           int32_t* sorted_pair, int32_t* pair_pos, void* x_perm, void* x_perm_scale,

@@ -101,7 +101,7 @@ SharedSplit shared_split(const moe_config_t& c) {
 
 // Scratch layout; the same for every entry point so one size serves all of them.
 struct Layout {
-  size_t logits, gate_partial, hist, tiles_l, tiles_s, h, h_scale, h_shared, sh_out, sh_part, idx, w, offsets, sorted,
+  size_t route, hist, tiles_l, tiles_s, h, h_scale, h_shared, sh_out, sh_part, idx, w, offsets, sorted,
       pos, xq, xq_scale, y_perm, xn, total;
 };
 
@@ -111,9 +111,7 @@ Layout layout(const moe_config_t& c) {
   const int64_t SI = int64_t(c.num_shared) * c.shared_intermediate;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += align256(std::max<size_t>(bytes, 1)); return at; };
-  L.logits = take(size_t(T * E * 4));
-  const int ks = gate_ksplit(c);
-  L.gate_partial = take(ks > 1 ? size_t(ks) * T * E * 8 : 0);
+  L.route = take(route_workspace_bytes(c));
   L.hist = take(size_t(int64_t(perm_blocks(int(P))) * E * 4));
   const FfnPlan fp = ffn_plan(c);
   L.tiles_l = take(size_t((2 * int64_t(fp.max_l) + 1) * 4));
@@ -415,7 +413,7 @@ static hipError_t forward_impl(const moe_config_t& c, const void* x, const void*
   void* xq_scale = act_scaled(c) ? at<void>(ws, L.xq_scale) : nullptr;
   void* y_perm = at<void>(ws, L.y_perm);
   int32_t* sorted = at<int32_t>(ws, L.sorted);
-  hipError_t e = launch_route(c, x, gate_w, bias, idx, w, at<float>(ws, L.logits), at<double>(ws, L.gate_partial), st);
+  hipError_t e = launch_route(c, x, gate_w, bias, idx, w, at<void>(ws, L.route), st);
   // Fused gather: the routed GEMMs read the token rows of x (or of its quantised
   // copy, made once per token) through the sorted pair order, with no gathered copy.
   if (e == hipSuccess) e = launch_permute(c, idx, x, offsets, sorted, pos, nullptr, nullptr, at<int32_t>(ws, L.hist), st);
@@ -498,8 +496,8 @@ moe_status_t moe_route(const moe_config_t* cfg, const void* x, const float* gate
   if (s != MOE_OK || cfg->num_tokens == 0) return s;
   if (!x || !gate_w || !bias || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARGUMENT;
   const Layout L = layout(*cfg);
-  return to_status(launch_route(*cfg, x, gate_w, bias, topk_idx, topk_w, at<float>(ws, L.logits),
-                                at<double>(ws, L.gate_partial), static_cast<hipStream_t>(stream)));
+  return to_status(launch_route(*cfg, x, gate_w, bias, topk_idx, topk_w, at<void>(ws, L.route),
+                                static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_permute(const moe_config_t* cfg, const int32_t* topk_idx, const void* x, int32_t* expert_offsets,

@@ -16,6 +16,79 @@ from workloads import generate as G
 TOL = {C.RECIPE_F32: 1e-5, C.RECIPE_BF16: 2e-2, C.RECIPE_FP8_B128: 6e-2, C.RECIPE_MXFP4: 6e-2, C.RECIPE_NVFP4: 6e-2}
 
 
+# The library screens the gate logits on the bf16 MFMA pipe when the activations are
+# bf16 and there are at least this many tokens; picks whose rank the screen leaves
+# in no doubt then take their weight from the screened logit.
+SCREEN_MIN_TOKENS = 512
+
+
+def gate_screened(cfg) -> bool:
+    return cfg.recipe != C.RECIPE_F32 and cfg.num_tokens >= SCREEN_MIN_TOKENS
+
+
+def _bf16_rn(v32: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(v32, dtype=np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def _ulp32(v: np.ndarray) -> np.ndarray:
+    a = np.abs(np.asarray(v, dtype=np.float32))
+    return np.spacing(np.maximum(a, np.float32(2.0 ** -126))).astype(np.float64)
+
+
+def screened_weight_bound(cfg, x64: np.ndarray, gate_w: np.ndarray, ref: dict) -> np.ndarray:
+    """Per pick, the largest |w - w_exact| for a weight computed from a screened logit.
+
+    The screen splits each fp32 gate weight (round to nearest) into two bf16 pieces
+    and a remainder, w = w1 + w2 + w3, and adds the exact products with the pieces in
+    fp32 (256 per accumulator group, then the groups); its logit is within
+    eps = gamma_n |x|_2 (|w1|_2 + |w2|_2) + |x|_2 |w3|_2 of the exact one, with
+    n = 256 + H/128 + 2 (the most groups any K split has).  The score is then within
+    lip (eps + ulp(l)) + ulp(s), lip = 1/4 (sigmoid) or 0.32 (sqrt(softplus)), and the
+    normalised, scaled weights move by at most the first-order sum below plus two
+    roundings."""
+    w32 = np.asarray(gate_w, dtype=np.float32)
+    w1 = _bf16_rn(w32)
+    r = (w32 - w1).astype(np.float32)
+    w2 = _bf16_rn(r)
+    w3 = (r - w2).astype(np.float32)
+    n12 = np.linalg.norm(w1.astype(np.float64), axis=1) + np.linalg.norm(w2.astype(np.float64), axis=1)
+    n3 = np.linalg.norm(w3.astype(np.float64), axis=1)
+    xn = np.linalg.norm(x64, axis=1)
+    u, n = 2.0 ** -24, 256 + cfg.hidden // 128 + 2
+    gam = n * u / (1 - n * u)
+    lip = 0.25 if cfg.score_func == C.SCORE_SIGMOID else 0.32
+    idx = ref["idx"]
+    eps = gam * xn[:, None] * n12[idx] + xn[:, None] * n3[idx]
+    logit = np.take_along_axis(ref["logits"], idx, axis=1)
+    s = np.take_along_axis(ref["s"], idx, axis=1).astype(np.float64)
+    ds = lip * (eps + _ulp32(logit)) + _ulp32(s)
+    scale = float(cfg.routed_scaling_factor)
+    if cfg.norm_topk_prob:
+        S = s.sum(axis=1, keepdims=True)
+        dw = scale * (ds / S + s * ds.sum(axis=1, keepdims=True) / S ** 2)
+    else:
+        dw = scale * ds
+    return dw * 1.001 + 2 * _ulp32(ref["w"])
+
+
+def check_routing(cfg, idx: np.ndarray, w: np.ndarray, ref: dict, x64=None, gate_w=None):
+    """Indices bit-exact; weights to 1e-6 relative, or, for a screened gate, within
+    screened_weight_bound with a median relative error below 1e-6."""
+    bad = np.nonzero((idx != ref["idx"]).any(axis=1))[0]
+    assert bad.size == 0, f"{bad.size} tokens routed differently, first {bad[:5]}: {idx[bad[:2]]} vs {ref['idx'][bad[:2]]}"
+    if not gate_screened(cfg):
+        np.testing.assert_allclose(w, ref["w"], rtol=1e-6, atol=0)
+        return
+    bound = screened_weight_bound(cfg, x64, gate_w, ref)
+    dev = np.abs(w.astype(np.float64) - ref["w"].astype(np.float64))
+    worst = np.unravel_index(np.argmax(dev / bound), dev.shape)
+    assert np.all(dev <= bound), f"weight {worst}: |dw| {dev[worst]:.3e} > bound {bound[worst]:.3e}"
+    rel = dev / np.abs(ref["w"]).astype(np.float64)
+    print(f"screened weights: median rel {np.median(rel):.2e}, max rel {rel.max():.2e}, "
+          f"max dev/bound {float((dev / bound).max()):.3f}")
+    assert np.median(rel) < 1e-6
+
+
 def to_np(t: torch.Tensor) -> np.ndarray:
     """Device tensor -> numpy in its storage form (bf16 as uint16 bit patterns)."""
     t = t.detach()

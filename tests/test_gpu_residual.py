@@ -19,6 +19,10 @@ RESIDUAL = [C.TINY_F32, C.MINI_F32, C.MINI_GROUPED_BF16, C.MINI_DECODE_BF16, C.M
             C.MINI_MXFP4]
 
 
+def _normed(inp):
+    return O.rms_norm(HN.x_f64(inp), inp.norm_w.cpu().numpy(), G.RMS_EPS, inp.cfg.recipe)
+
+
 def _oracle(inp, tokens=None):
     s13, s2 = HN.shared_f64(inp)
     return O.moe_forward_residual(inp.cfg, HN.x_f64(inp), inp.norm_w.cpu().numpy(), G.RMS_EPS,
@@ -54,7 +58,7 @@ def test_forward_residual_parity(cfg):
     inp = G.generate(cfg, device="cuda")
     b, out = _run(inp)
     ref = _oracle(inp)
-    _check_routing(b, ref)
+    _check_routing(b, ref, inp, _normed(inp))
     err = HN.rel_l2(HN.out_f64(out), ref["out"])
     assert err < HN.TOL[cfg.recipe], f"out rel-L2 {err:.3e}"
     # the residual is really there: the result differs from the MoE output alone
@@ -72,7 +76,7 @@ def test_forward_residual_full_size_decode():
     b, out = _run(inp)
     tokens = HN.sample_tokens(cfg.num_tokens, 24)
     ref = _oracle(inp, tokens=tokens)
-    _check_routing(b, ref)
+    _check_routing(b, ref, inp, _normed(inp))
     got = HN.out_f64(out[torch.from_numpy(tokens).cuda()])
     err = HN.rel_l2(got, ref["out"])
     rows = HN.row_rel_l2(got, ref["out"])
