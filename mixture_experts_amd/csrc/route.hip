@@ -185,12 +185,21 @@ __device__ __forceinline__ double score_d(double z, int func) {   // sigmoid or 
 
 __device__ __forceinline__ float score_fp64(float logit, int func) { return float(score_d(double(logit), func)); }
 
-// The same in fp32 arithmetic: within a few units in the last place of the exact
-// score (one exp, one log1p or division, one sqrt, a rounding each).
-__device__ __forceinline__ float score_f32(float z, int func) {
+// The score and its slope f'(z) in fp32 arithmetic, each within a few units in the
+// last place (one exp, one log1p or division, one sqrt, a rounding each).  Both
+// functions increase, with f' <= 0.32 and |f''| < 0.1 everywhere (sigmoid:
+// sigma (1 - sigma) and its derivative; sqrt(softplus): sigma / (2 f)).
+__device__ __forceinline__ void score_slope_f32(float z, int func, float& s, float& slope) {
   const float ez = expf(-fabsf(z));
-  if (func == MOE_SCORE_SIGMOID) return z >= 0.0f ? 1.0f / (1.0f + ez) : ez / (1.0f + ez);
-  return sqrtf(fmaxf(z, 0.0f) + log1pf(ez));
+  const float sig = z >= 0.0f ? 1.0f / (1.0f + ez) : ez / (1.0f + ez);
+  if (func == MOE_SCORE_SIGMOID) {
+    s = sig;
+    slope = sig * (1.0f - sig);
+  } else {
+    s = sqrtf(fmaxf(z, 0.0f) + log1pf(ez));
+    slope = s > 0.0f ? sig / (2.0f * s) : 0.32f;
+    slope = slope < 0.32f ? slope : 0.32f;           // (also when the quotient is not finite)
+  }
 }
 
 constexpr int RT_WAVES = 4;
@@ -330,8 +339,8 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ l
 // lip * (eps + ulp) + ulp of the exact one (lip = 1/4 for sigmoid, < 0.32 for
 // sqrt(softplus)).
 // ---------------------------------------------------------------------------
-constexpr int SCT = 128, SCE = 128, SK = 32, SGRP = 4;
-constexpr int SC_BLOCKS_PER_CU = 2;
+constexpr int SCT = 256, SCE = 128, SK = 32, SGRP = 4;
+constexpr int SC_WAVES = SCT / 32;                 // (SCT / 64) x 2 waves of 64 x 64
 
 __device__ __forceinline__ uint32_t bf16_rn(float f) {   // round to nearest even; inf / nan stay inf / nan
   const uint32_t u = __float_as_uint(f);
@@ -340,13 +349,14 @@ __device__ __forceinline__ uint32_t bf16_rn(float f) {   // round to nearest eve
 }
 
 // Pieces w1, w2 of every gate weight ([E][H] bf16 each) and per expert
-// wn[4e..4e+2] = |w1|_2 + |w2|_2, |w3|_2, |w|_2, each rounded up (one wave per expert).
+// wn[4e..4e+2] = |w1|_2 + |w2|_2, |w3|_2, |w|_2, each rounded up (one 256-thread block
+// per expert; fp64 sums of squares).
 __global__ __launch_bounds__(256) void gate_prep(const float* __restrict__ wg, int E, int H, uint16_t* __restrict__ w1,
                                                  uint16_t* __restrict__ w2, float* __restrict__ wn) {
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (e >= E) return;
+  __shared__ double red[4][4];
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   double s1 = 0.0, s2 = 0.0, s3 = 0.0, sw = 0.0;
-  for (int h = 4 * lane; h < H; h += 256) {
+  for (int h = 4 * tid; h < H; h += 1024) {
     const float4 v = *reinterpret_cast<const float4*>(wg + size_t(e) * H + h);
     const float wv[4] = {v.x, v.y, v.z, v.w};
     uint32_t p1[4], p2[4];
@@ -372,6 +382,17 @@ __global__ __launch_bounds__(256) void gate_prep(const float* __restrict__ wg, i
     sw += __shfl_xor(sw, off, 64);
   }
   if (lane == 0) {
+    red[wave][0] = s1;
+    red[wave][1] = s2;
+    red[wave][2] = s3;
+    red[wave][3] = sw;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    s1 = red[0][0] + red[1][0] + red[2][0] + red[3][0];
+    s2 = red[0][1] + red[1][1] + red[2][1] + red[3][1];
+    s3 = red[0][2] + red[1][2] + red[2][2] + red[3][2];
+    sw = red[0][3] + red[1][3] + red[2][3] + red[3][3];
     constexpr double up = 1.0 + 0x1p-20;              // covers the fp64 sums and the rounding to fp32
     wn[4 * e + 0] = float((sqrt(s1) + sqrt(s2)) * up);
     wn[4 * e + 1] = float(sqrt(s3) * up);
@@ -382,24 +403,31 @@ __global__ __launch_bounds__(256) void gate_prep(const float* __restrict__ wg, i
 
 typedef __attribute__((ext_vector_type(4))) float rf32x4;
 
-// Screened logits: a 128-token x 128-expert tile per 256-thread block, wave (wt, we)
-// owning tokens 64 wt .. and experts 64 we .. (4 x 4 MFMA 16x16x32 tiles).  K runs in
-// chunks of 32 through a ring of SC_NS LDS stages filled by direct global -> LDS
-// copies (16 bytes per lane, no registers), SC_NS - 1 chunks ahead of the one being
-// multiplied.  A stage holds 128 x rows, then 128 w1 rows, then 128 w2 rows of 64
-// bytes; the 16-byte segment s of row r sits in slot s ^ ((r >> 1) & 3): the MFMA
+// Screened logits: a 256-token x 128-expert tile per 512-thread block (one per CU),
+// wave (wt, we) owning tokens 64 wt .. and experts 64 we .. (4 x 4 MFMA 16x16x32
+// tiles).  K runs in chunks of 32 through a ring of SC_NS LDS stages filled by direct
+// global -> LDS copies (16 bytes per lane, no registers), SC_NS - 1 chunks ahead of
+// the one being multiplied.  A stage holds 256 x rows, then 128 w1 rows, then 128 w2
+// rows of 64 bytes; the 16-byte segment s of row r sits in slot s ^ ((r >> 1) & 3): the MFMA
 // operand reads (16 rows, one segment per 16 lanes) are then free of bank conflicts
 // (measured: SQ_LDS_BANK_CONFLICT is zero for this pattern and 4 cycles per read
-// for the unswizzled rows, for s ^ ((r >> 2) & 3) and for 80-byte padded rows).  Blocks are dealt to
-// the 8 XCDs in turn, so logical tile i*N/8 + j runs on XCD i: the expert tiles of one
-// token tile, which read the same x rows, share an L2.  part[split][t][e]: the
-// split's fp32 total.
-constexpr int SC_NS = 3;
-constexpr int SC_STAGE = (SCT + 2 * SCE) * SK * 2;   // 24 KiB
+// for the unswizzled rows, for s ^ ((r >> 2) & 3) and for 80-byte padded rows).
+// Blocks are dealt to the 8 XCDs in turn, so logical tile i*N/8 + j runs on XCD i:
+// the expert tiles of one token tile, which read the same x rows, share an L2.
+// part[split][t][e]: the split's fp32 total.  (Measured against 128 x 128 tiles,
+// two per CU, with 3 stages: 0.052 / 0.093 / 0.17 ms against 0.070 / 0.106 / 0.19 ms
+// for 8192 x 256, 4096 x 896 and 16384 x 384 at H = 7168.)
+constexpr int SC_NS = 4;
+constexpr int SC_STAGE = (SCT + 2 * SCE) * SK * 2;   // 32 KiB
+constexpr int SC_CPW = (SCT + 2 * SCE) / 16 / SC_WAVES;   // 16-row copies per wave and chunk
 
 typedef __attribute__((address_space(3))) void* sc_lds_ptr_t;
 
 __device__ __forceinline__ int sc_swz(int r, int seg) { return r * 64 + ((seg ^ ((r >> 1) & 3)) << 4); }
+
+__device__ __forceinline__ void sc_copy16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (sc_lds_ptr_t)lds, 16, 0, 0);
+}
 
 template <int N>
 __device__ __forceinline__ void sc_wait_vmcnt() {
@@ -407,7 +435,7 @@ __device__ __forceinline__ void sc_wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
 }
 
-__global__ __launch_bounds__(256, SC_BLOCKS_PER_CU) void gate_screen(
+__global__ __launch_bounds__(SCT * 2, 1) void gate_screen(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w2,
     float* __restrict__ part, float* __restrict__ xsq, int T, int E, int H, int kchunk, int e_tiles, int tiles) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[SC_NS][SC_STAGE];
@@ -418,27 +446,27 @@ __global__ __launch_bounds__(256, SC_BLOCKS_PER_CU) void gate_screen(
   const int split = lg / tiles, rest = lg % tiles;
   const int t0 = (rest / e_tiles) * SCT, e0 = (rest % e_tiles) * SCE;
   const int kbeg = split * kchunk, nch = kchunk / SK;
-  // copies of one chunk: wave w fills 16-row blocks 2w, 2w+1 of x, w1 and w2; lane l
-  // takes row l >> 2 of the block and the segment stored in its slot l & 3.  Rows
-  // past T / E read the last row (their results are dropped).
+  // copies of one chunk: wave w fills 16-row blocks SC_CPW w .. of the stage (x rows,
+  // then w1, then w2); lane l takes row l >> 2 of the block and the segment stored in
+  // its slot l & 3.  Rows past T / E read the last row (their results are dropped).
   const int lr = lane >> 2, lseg = (lane & 3) ^ ((lane >> 3) & 3);
-  const char* src[6];
-  int dst[6];
+  const char* src[SC_CPW];
+  int dst[SC_CPW];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int q = 2 * wave + i, r = 16 * q + lr;
-    src[i] = reinterpret_cast<const char*>(x + size_t(min(t0 + r, T - 1)) * H + kbeg) + lseg * 16;
-    const size_t wr = size_t(min(e0 + r, E - 1)) * H + kbeg;
-    src[2 + i] = reinterpret_cast<const char*>(w1 + wr) + lseg * 16;
-    src[4 + i] = reinterpret_cast<const char*>(w2 + wr) + lseg * 16;
-    dst[i] = q * 1024;
-    dst[2 + i] = SCT * 64 + q * 1024;
-    dst[4 + i] = (SCT + SCE) * 64 + q * 1024;
+  for (int i = 0; i < SC_CPW; ++i) {
+    const int blk = wave * SC_CPW + i;
+    if (blk < SCT / 16) {
+      src[i] = reinterpret_cast<const char*>(x + size_t(min(t0 + 16 * blk + lr, T - 1)) * H + kbeg) + lseg * 16;
+    } else {
+      const int bb = blk - SCT / 16, r = 16 * (bb % (SCE / 16)) + lr;
+      const uint16_t* w = bb < SCE / 16 ? w1 : w2;
+      src[i] = reinterpret_cast<const char*>(w + size_t(min(e0 + r, E - 1)) * H + kbeg) + lseg * 16;
+    }
+    dst[i] = blk * 1024;
   }
   auto issue = [&](int c, int slot) {
 #pragma unroll
-    for (int j = 0; j < 6; ++j)
-      __builtin_amdgcn_global_load_lds(src[j] + c * 64, (sc_lds_ptr_t)(&ring[slot][0] + dst[j]), 16, 0, 0);
+    for (int j = 0; j < SC_CPW; ++j) sc_copy16(src[j] + c * 64, &ring[slot][0] + dst[j]);
   };
   rf32x4 cur[4][4], tot[4][4];
   const rf32x4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -455,11 +483,11 @@ __global__ __launch_bounds__(256, SC_BLOCKS_PER_CU) void gate_screen(
     }
   // Every iteration issues one chunk's copies (past the end: chunk nch-1 again, into
   // a slot no later iteration reads), so the count of this wave's copies newer than
-  // chunk c's is always 6 (SC_NS - 2).
+  // chunk c's is always SC_CPW (SC_NS - 2).
 #pragma unroll
   for (int c = 0; c < SC_NS - 1; ++c) issue(min(c, nch - 1), c);
   for (int c = 0; c < nch; ++c) {
-    sc_wait_vmcnt<6 * (SC_NS - 2)>();
+    sc_wait_vmcnt<SC_CPW * (SC_NS - 2)>();
     // every wave's copies of chunk c are in LDS, and every wave is done with slot
     // (c - 1) % SC_NS, which the next copies fill
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -626,32 +654,29 @@ __global__ __launch_bounds__(256, 2) void router_screen_kernel(
     double zs = 0.0;
     for (int q = 0; q < nsplit; ++q) zs += double(part[(size_t(q) * T + t) * E + e]);
     const float l32 = float(zs);
-    const float s = score_fp64(l32, func);
-    const float key = selection_key(s, bias[e]);
     const float4 n = *reinterpret_cast<const float4*>(wn + 4 * e);
     const double eps = gam * xnorm * double(n.x) + xnorm * double(n.y) + sub * (xnorm + double(n.z)) + 0x1p-100;
-    // The exact fp32 logit is within dl of zs (twice the bound, for whatever rounding
-    // the MFMA sums use, and two fp32 roundings).  Both score functions increase, so
-    // the exact score lies between the scores of the ends zs -/+ dl (rounded outward
-    // to fp32), which are evaluated in fp32 and widened by 2^-16 relative, far more
-    // than that evaluation's error; the exact key, an fp32 sum with the bias, lies
-    // between the same sums of those ends.
+    // The exact fp32 logit is within dl of l32 (twice the bound, for whatever rounding
+    // the MFMA sums use, and two fp32 roundings).  By the mean value theorem (twice)
+    // the exact score is then within (f'(l32) + 0.125 dl) dl of f(l32); the fp32
+    // evaluation adds at most 2^-16 relative (far more than its error) and the
+    // rounding of the exact score one unit.  The exact key, an fp32 sum with the
+    // bias, lies between the same sums of the score interval's ends.
     const double dl = 2.0 * eps + 2.0 * double(ulp32(l32));
-    float zlo = float(zs - dl), zhi = float(zs + dl);
-    zlo -= ulp32(zlo);
-    zhi += ulp32(zhi);
-    const float slo = score_f32(zlo, func) * (1.0f - 0x1p-16f), shi = score_f32(zhi, func) * (1.0f + 0x1p-16f);
-    const float klo = slo + bias[e], khi = shi + bias[e];
+    float sc, slope;
+    score_slope_f32(l32, func, sc, slope);
+    const float hw = float((double(slope) * (1.0 + 0x1p-10) + 0.125 * dl) * dl) + sc * 0x1p-16f + ulp32(sc);
+    const float u = ulp32(fmaxf(sc, hw));
+    const float klo = ((sc - hw) - u) + bias[e], khi = ((sc + hw) + u) + bias[e];
     const float lo = klo - ulp32(klo), hi = khi + ulp32(khi);
-    if (!(dl < INFINITY) || !(fabs(zs) < INFINITY) || key == -INFINITY || !(lo == lo) || !(hi == hi)) {
+    if (!(dl < INFINITY) || !(fabs(zs) < INFINITY) || !(lo > -INFINITY) || !(hi == hi) || hi == INFINITY) {
       LO[e] = -INFINITY;                             // NaN, infinity or overflow: recompute
       HI[e] = INFINITY;
     } else {
       LO[e] = lo;
       HI[e] = hi;
     }
-    KX[e] = key;                                     // screened key and score until recomputed
-    SX[e] = s;
+    SX[e] = l32;                                     // the screened logit (its score: when listed)
     ST[e] = 0u;
   }
   auto recompute = [&]() {                           // exact keys of the requested experts
@@ -820,6 +845,11 @@ __global__ __launch_bounds__(256, 2) void router_screen_kernel(
       has = has && HI[ce] >= from_orderable(best);
     }
     const bool ex = has && (ST[ce] & 1u);
+    if (has && !ex) {                                // screened score and key (inside [LO, HI])
+      const float sc = score_fp64(SX[ce], func);
+      SX[ce] = sc;
+      KX[ce] = selection_key(sc, bias[ce]);
+    }
     const float lo = has ? (ex ? KX[ce] : LO[ce]) : -INFINITY;   // lanes without a candidate: never above,
     const float hi = has ? (ex ? KX[ce] : HI[ce]) : -INFINITY;   // and out
     int above = 0;
@@ -903,14 +933,13 @@ static int gate_ksplit_f64(const moe_config_t& c) {
   return best;
 }
 
-// Screen: bf16-MFMA bound, one 128 x 128 block per CU at full rate (two share a CU
-// at half rate each), so time ~ ceil(blocks / 256) * (K/d chunks) * t_chunk; every
-// split beyond the first adds a T x E fp32 partial written and read once.  Splits
-// keep >= 8 chunks each.
+// Screen: one 256 x 128 block per CU, about 0.93 us per 32-deep chunk (measured), so
+// time ~ ceil(blocks / 256) * (K/d chunks) * t_chunk; every split beyond the first
+// adds a T x E fp32 partial written and read once.  Splits keep >= 8 chunks each.
 static int gate_ksplit_screen(const moe_config_t& c) {
   const int64_t tiles = int64_t((c.num_experts + SCE - 1) / SCE) * ((c.num_tokens + SCT - 1) / SCT);
   const int steps = c.hidden / SK;
-  constexpr double chunk_s = 0.22e-6, bytes_per_s = 5e12;
+  constexpr double chunk_s = 0.93e-6, bytes_per_s = 5e12;
   int best = 1;
   double best_t = 0.0;
   for (int d = 1; d <= 32 && d <= steps; ++d) {
@@ -1003,8 +1032,8 @@ hipError_t launch_route(const moe_config_t& c, const void* x, const float* gate_
   const int kchunk = H / ks, e_tiles = (E + SCE - 1) / SCE, tiles = e_tiles * ((T + SCT - 1) / SCT);
   {
     ProfScope p(MOE_K_GATE, st);
-    gate_prep<<<(E + 3) / 4, 256, 0, st>>>(gate_w, E, H, w1, w2, wn);
-    gate_screen<<<tiles * ks, 256, 0, st>>>(xb, w1, w2, part, xsq, T, E, H, kchunk, e_tiles, tiles);
+    gate_prep<<<E, 256, 0, st>>>(gate_w, E, H, w1, w2, wn);
+    gate_screen<<<tiles * ks, SCT * 2, 0, st>>>(xb, w1, w2, part, xsq, T, E, H, kchunk, e_tiles, tiles);
   }
   // error bound factor: gamma_n with n = 256 (one accumulator group) + groups + 2
   const int groups = (kchunk / SK + SGRP - 1) / SGRP;

@@ -149,3 +149,48 @@ def test_the_accumulation_term_is_needed():
     err = abs(Fraction(_screen(x, w, "forward")) - exact)
     assert err > 0
     assert err <= Fraction(acc_part)
+
+
+def _score64(z, sigmoid):
+    z = np.asarray(z, dtype=np.float64)
+    ez = np.exp(-np.abs(z))
+    sig = np.where(z >= 0, 1 / (1 + ez), ez / (1 + ez))
+    return sig if sigmoid else np.sqrt(np.maximum(z, 0) + np.log1p(ez))
+
+
+def test_score_second_derivatives_are_below_a_tenth():
+    """The router widens a score interval by 0.125 dl^2 for the change of slope: both
+    score functions have |f''| < 0.1 (finite differences over [-60, 60])."""
+    z = np.linspace(-60, 60, 1_200_001)
+    h = 1e-3
+    for sigmoid in (True, False):
+        f2 = (_score64(z + h, sigmoid) - 2 * _score64(z, sigmoid) + _score64(z - h, sigmoid)) / h ** 2
+        assert np.abs(f2).max() < 0.1
+    # and f' <= 0.32 for sqrt(softplus), 0.25 for sigmoid
+    f1 = (_score64(z + h, False) - _score64(z - h, False)) / (2 * h)
+    assert f1.max() < 0.32 and f1.min() > 0
+
+
+def test_one_evaluation_score_interval_holds_the_scores_around_it():
+    """The key interval of one screened logit: f(l32) and its slope in fp32, widened by
+    (slope (1 + 2^-10) + 0.125 dl) dl + 2^-16 f + ulp, contains the fp32 score of every
+    logit within dl (sampled densely), for both score functions and dl from 1e-6 to 1."""
+    rng = np.random.default_rng(5)
+    for sigmoid in (True, False):
+        for _ in range(400):
+            l32 = np.float32(rng.normal() * rng.choice([0.5, 3.0, 12.0]))
+            dl = float(10.0 ** rng.uniform(-6, 0))
+            ez = np.float32(np.exp(np.float32(-abs(l32))))
+            sig = np.float32(1) / (np.float32(1) + ez) if l32 >= 0 else ez / (np.float32(1) + ez)
+            if sigmoid:
+                sc, slope = np.float32(sig), np.float32(sig * (np.float32(1) - sig))
+            else:
+                sc = np.float32(np.sqrt(np.float32(max(l32, 0)) + np.float32(np.log1p(ez))))
+                slope = np.float32(min(sig / (np.float32(2) * sc), 0.32)) if sc > 0 else np.float32(0.32)
+            hw = np.float32((float(slope) * (1 + 2 ** -10) + 0.125 * dl) * dl) + sc * np.float32(2 ** -16) \
+                + np.spacing(sc)
+            u = np.spacing(np.float32(max(sc, hw)))
+            lo, hi = np.float32(np.float32(sc - hw) - u), np.float32(np.float32(sc + hw) + u)
+            zz = float(l32) + np.linspace(-dl, dl, 2001)
+            s = _score64(zz, sigmoid).astype(np.float32)
+            assert np.all(s >= lo) and np.all(s <= hi), (sigmoid, l32, dl)
