@@ -12,7 +12,9 @@ I=2048, one shared expert, bf16):
   every launch on its stream;
 - `configs`: the prefill shapes (bf16 grouped top-k, MXFP4, skewed fp8) measured
   the same way in the same run, each with its gate/up and routed-GEMM (gate/up +
-  down) fractions of the MFMA / HBM peak and the layer's fraction of its roofline;
+  down) fractions of the binding peak -- HBM for the algorithmic bytes or MFMA for
+  the flops, whichever takes longer at its peak, the other fraction beside it --
+  and the layer's fraction of its roofline;
 - `cpu_baseline`: the CPU oracle on the decode workload (see cpu_baseline()).
 """
 from __future__ import annotations
@@ -33,7 +35,6 @@ PEAK = {  # MI355X published dense peaks
     "bf16_TFLOPs": 2516.6, "fp16_TFLOPs": 2516.6, "fp8_TFLOPs": 5033.2, "mxfp4_TFLOPs": 10066.3, "fp32_TFLOPs": 157.3,
 }
 EXTRA_CONFIGS = ("prefill_bf16_grouped", "finegrained_mxfp4", "skewed_fp8")
-HBM_BOUND = ("decode_bf16", "finegrained_mxfp4", "tiny_fp32", "decode_nvfp4")
 
 
 def parse():
@@ -172,28 +173,35 @@ def run_workload(cfg, args, residual=False):
     return inp, b, ms_step, ms_step_instr, prof
 
 
+def _bound(bytes_, flops, t_s, recipe):
+    """The binding roofline of a step: HBM (algorithmic bytes) or MFMA (flops), whichever
+    takes longer at its peak; the other one's fraction is reported beside it."""
+    pk = mfma_peak(recipe)
+    hbm = {"bound": "hbm", "achieved": bytes_ / t_s / 1e9, "peak": PEAK["hbm_GBps"], "unit": "GB/s"}
+    mf = {"bound": "mfma", "achieved": flops / t_s / 1e12, "peak": pk, "unit": "TFLOP/s"}
+    for d in (hbm, mf):
+        d["achieved"] = round(d["achieved"], 1)
+        d["frac"] = round(d["achieved"] / d["peak"], 4)
+    t_hbm, t_mf = bytes_ / (PEAK["hbm_GBps"] * 1e9), flops / (pk * 1e12)
+    main, other = (hbm, mf) if t_hbm >= t_mf else (mf, hbm)
+    main["roofline_ms"] = round(max(t_hbm, t_mf) * 1e3, 4)
+    main["other"] = other
+    return main
+
+
 def fractions(cfg, counts, prof, steps):
     """Gate/up and routed (gate/up + down) fractions of the binding peak."""
     touched = int((counts > 0).sum())
-    hbm = cfg.name in HBM_BOUND
     ms_gu, n_gu = prof["ffn_gate_up"]
     ms_dn, n_dn = prof["ffn_down"]
     avg_gu = ms_gu / max(n_gu, 1)
     gu_bytes, gu_flops = gate_up_work(cfg, touched)
     r_bytes, r_flops = routed_work(cfg, touched)
     t_routed = (ms_gu + ms_dn) / steps * 1e-3
-    if hbm:
-        gu = {"bound": "hbm", "achieved": gu_bytes / (avg_gu * 1e-3) / 1e9, "peak": PEAK["hbm_GBps"], "unit": "GB/s"}
-        rt = {"bound": "hbm", "achieved": r_bytes / t_routed / 1e9, "peak": PEAK["hbm_GBps"], "unit": "GB/s"}
-    else:
-        pk = mfma_peak(cfg.recipe)
-        gu = {"bound": "mfma", "achieved": gu_flops / (avg_gu * 1e-3) / 1e12, "peak": pk, "unit": "TFLOP/s"}
-        rt = {"bound": "mfma", "achieved": r_flops / t_routed / 1e12, "peak": pk, "unit": "TFLOP/s"}
-    for d in (gu, rt):
-        d["achieved"] = round(d["achieved"], 1)
-        d["frac"] = round(d["achieved"] / d["peak"], 4)
+    gu = _bound(gu_bytes, gu_flops, avg_gu * 1e-3, cfg.recipe)
+    rt = _bound(r_bytes, r_flops, t_routed, cfg.recipe)
     gu["avg_launch_ms"] = round(avg_gu, 4)
-    gu["algorithmic_per_launch"] = gu_bytes if hbm else gu_flops
+    gu["algorithmic_per_launch"] = gu_bytes if gu["bound"] == "hbm" else gu_flops
     rt["ms_per_step"] = round(t_routed * 1e3, 4)
     return touched, gu, rt
 
