@@ -313,7 +313,7 @@ def main():
     counts = np.bincount(b.topk_idx.cpu().numpy().reshape(-1), minlength=cfg.num_experts)
     touched, gu, rt = fractions(cfg, counts, prof, args.steps)
     src_hash = kernel_source_hash()
-    roof = {k: gu[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    roof = {k: gu[k] for k in ("bound", "achieved", "peak", "unit", "frac", "roofline_ms", "other")}
     roof["traffic"] = traffic_from_profiles(cfg.name, src_hash)
     roof.update(kernel="ffn_gate_up", avg_launch_ms=gu["avg_launch_ms"],
                 algorithmic_per_launch=gu["algorithmic_per_launch"], routed_gate_up_down=rt)
