@@ -165,9 +165,21 @@ size_t moe_workspace_bytes(const moe_config_t* cfg);
  *   Out: topk_idx [T][k] int32 in selection order (key = fp32(score + bias)
  *   descending, ties to the lower expert index), topk_w [T][k] fp32 = the
  *   unbiased scores of the picks normalised to sum 1 (when norm_topk_prob),
- *   times routed_scaling_factor.  Logits are the fp32 rounding of the dot
- *   products evaluated with exact products and fp64 accumulation; scores are
- *   fp32 roundings of the fp64 score function. */
+ *   times routed_scaling_factor.
+ *   Selection and order are those of the exact gate: logits = the fp32 rounding
+ *   of the dot products evaluated with exact products and fp64 accumulation,
+ *   scores = fp32 roundings of the fp64 score function.  With fp32 activations,
+ *   or bf16 activations and fewer than 512 tokens, the gate is computed that way
+ *   (fp64 MFMA) and the weights use those exact scores.  With bf16 activations and
+ *   512 tokens or more the logits are screened on the bf16 MFMA pipe (each fp32
+ *   gate weight split into two bf16 pieces and a remainder, w = w1 + w2 + w3, exact
+ *   products, fp32 sums) within eps = gamma_n |x|_2 (|w1|_2 + |w2|_2) + |x|_2 |w3|_2
+ *   of the exact dot product (n = 256 + accumulator groups + 2, gamma_n =
+ *   n 2^-24 / (1 - n 2^-24), for sums rounding to within 2^-24 relative; the
+ *   router allows twice eps), and every expert whose rank that leaves open is
+ *   recomputed exactly; a pick whose rank is never in doubt keeps the score of
+ *   its screened logit for its weight, within 0.32 (eps + 2 ulp) + ulp of the
+ *   exact score. */
 moe_status_t moe_route(const moe_config_t* cfg, const void* x, const float* gate_w,
                        const float* bias, int32_t* topk_idx, float* topk_w,
                        void* ws, size_t ws_bytes, void* stream);
@@ -315,7 +327,7 @@ const char* moe_status_string(moe_status_t status);
  * Not thread-safe; meant for benchmarks and profiling runs.
  * ------------------------------------------------------------------------ */
 typedef enum {
-  MOE_K_GATE = 0,              /* gate logits (fp64-accumulated FP32 linear)          */
+  MOE_K_GATE = 0,              /* gate logits (fp64 MFMA, or the bf16 screen)          */
   MOE_K_ROUTER,                /* score, bias, grouped top-k, weights                 */
   MOE_K_PERM_HIST,             /* counting sort: per-chunk expert histograms          */
   MOE_K_PERM_SCAN,             /* counting sort: prefix sums, expert offsets          */
