@@ -5,6 +5,12 @@
 // 3.2 + e_score_correction_bias, group top-2 sums, keep topk_group groups, top-k;
 // 3.3 normalise the k picked scores to sum 1, times routed_scaling_factor.
 // sqrtsoftplus is the DeepSeek-V4-Pro score (lzwjava.github.io, architecture).
+//
+// Two gate paths with the same selection, that of the exact logits (the fp32
+// rounding of fp64-accumulated dot products): the fp64-MFMA gate and its router
+// (fp32 activations, and bf16 below 512 tokens), and the bf16-MFMA screen with an
+// exact recompute of the experts its error bound leaves open (bf16, 512 tokens or
+// more).
 #include <algorithm>
 #include <type_traits>
 
