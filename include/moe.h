@@ -29,7 +29,11 @@
  * Conventions for every entry point
  *   - Every buffer pointer is a DEVICE pointer owned by the caller; the library
  *     never allocates, frees or copies to the host, and never synchronises.
- *     Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *     Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) as
+ *     kernel launches only (no memset or copy), so a call can be captured into a
+ *     HIP graph and replayed; make one call outside the capture first, which
+ *     does the library's first-use work (loading the kernels; the no-alloc
+ *     entry's scratch lookup).
  *   - Inputs are never written (except an `out` that the caller makes the same
  *     buffer as `resid`).  Outputs are fully overwritten.
  *   - Tensor pointers are 16-byte aligned (rows are read in 16-byte pieces);
