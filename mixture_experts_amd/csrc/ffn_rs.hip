@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     else a_src[j] = A + off;
   }
   const int sa_row = ASC ? a_row(g, ti.row0 + min(tid % BM, ti.rows - 1)) : 0;
-  auto load_sa = [&](int k0) -> SaT {            // every thread loads (rows clamped): equal vmcnt per wave
+  auto load_sa = [&](int k0) -> SaT {            // (rows clamped)
     if constexpr (MX)
       return *reinterpret_cast<const SaT*>(static_cast<const uint8_t*>(g.A_scale) + size_t(sa_row) * (K / 32) + k0 / 32);
     else
@@ -298,7 +298,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     for (int j = 0; j < A_INSTR; ++j)
       if constexpr (BUF) rs_bcopy16(A, a_src[j], uint32_t(k0 * EA), &As[buf][(wave * A_INSTR + j) * 1024]);
       else rs_copy16(a_src[j] + size_t(k0) * EA, &As[buf][(wave * A_INSTR + j) * 1024]);
-    if (ASC) sreg[buf] = load_sa(k0);
+    // fp8 with a two-stage ring (whose waits are vmcnt(0)): only the threads that
+    // stage a row scale load it.  Otherwise every thread loads one, so that counted
+    // waits match across waves (MXFP4 measured no faster with fewer loads).
+    if (ASC && (!FP8 || NST >= 3 || tid < BM)) sreg[buf] = load_sa(k0);
     // every wave loads (inactive column waves read a clamped, valid row) so that all
     // waves count the same loads per stage
 #pragma unroll
