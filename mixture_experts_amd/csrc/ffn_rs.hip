@@ -118,6 +118,13 @@ __device__ __forceinline__ f16x8 e2m1x8_to_f16(uint32_t w, NvScale sc) {
   return f16x8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
 }
 
+// Activation ring storage in LDS, one variable per (size, ID) instantiation.
+template <int N, int ID>
+__device__ __forceinline__ uint8_t* rs_lds_slot() {
+  __shared__ __attribute__((aligned(1024))) uint8_t a[N];
+  return a;
+}
+
 __device__ __forceinline__ i32x8 rs_cat(uint4 lo, uint4 hi) {
   return i32x8{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
 }
@@ -183,7 +190,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   using SaT = std::conditional_t<MX && KS == 256, uint2, uint32_t>;
   using SbT = std::conditional_t<NV, uint2, std::conditional_t<KS == 256, uint32_t, uint16_t>>;
   static_assert(size_t(NST) * BM * (AROWB + sizeof(SaT)) + 4 * BM * 4 <= 160 * 1024, "LDS budget");
-  __shared__ __attribute__((aligned(1024))) uint8_t As[NST][BM * AROWB];
+  // fp8: one LDS variable per activation ring slot, so that the compiler knows
+  // the copies into the next slot do not write the one being read and does not
+  // wait for them before the stage's LDS reads.  (The other recipes keep one
+  // ring array: split, they measured no faster, and MXFP4 spilled more.)
+  constexpr int SLOT = BM * AROWB;
+  static_assert(NST >= 2 && NST <= 3, "two or three ring slots");
+  auto As = [&](int b) -> uint8_t* {
+    if constexpr (FP8) {
+      if constexpr (NST >= 3)
+        return b == 0 ? rs_lds_slot<SLOT, 0>() : (b == 1 ? rs_lds_slot<SLOT, 1>() : rs_lds_slot<SLOT, 2>());
+      else
+        return b == 0 ? rs_lds_slot<SLOT, 0>() : rs_lds_slot<SLOT, 1>();
+    } else {
+      return rs_lds_slot<NST * SLOT, 3>() + b * SLOT;
+    }
+  };
   __shared__ SaT Sa[NST][BM];
   __shared__ float amax_lds[4][BM];
 
@@ -293,11 +315,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   uint4 breg[NST][2][BCH];
   SaT sreg[NST];
   SbT sbm[NST][2];
+  float sbf[NST][2];                               // fp8: the stage's two weight-block scales
   auto issue = [&](int k0, int buf) {
 #pragma unroll
     for (int j = 0; j < A_INSTR; ++j)
-      if constexpr (BUF) rs_bcopy16(A, a_src[j], uint32_t(k0 * EA), &As[buf][(wave * A_INSTR + j) * 1024]);
-      else rs_copy16(a_src[j] + size_t(k0) * EA, &As[buf][(wave * A_INSTR + j) * 1024]);
+      if constexpr (BUF) rs_bcopy16(A, a_src[j], uint32_t(k0 * EA), As(buf) + (wave * A_INSTR + j) * 1024);
+      else rs_copy16(a_src[j] + size_t(k0) * EA, As(buf) + (wave * A_INSTR + j) * 1024);
     // fp8 with a two-stage ring (whose waits are vmcnt(0)): only the threads that
     // stage a row scale load it.  Otherwise every thread loads one, so that counted
     // waits match across waves (MXFP4 measured no faster with fewer loads).
@@ -309,10 +332,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
       const uint8_t* p = bsrc(f, k0);
 #pragma unroll
       for (int c = 0; c < BCH; ++c) breg[buf][f][c] = *reinterpret_cast<const uint4*>(p + c * 16);
+      // the weight scales travel with their stage: a load issued at compute time,
+      // behind the next stage's weight loads, would make its wait cover those too
       if (FP4) sbm[buf][f] = bscale_fp4(f, k0);
+      if (FP8) sbf[buf][f] = bscale_fp8(f, k0);
     }
   };
-  constexpr int PER_STAGE = A_INSTR + (ASC ? 1 : 0) + 2 * BCH + (FP4 ? 2 : 0);   // loads per stage per thread
+  constexpr int PER_STAGE = A_INSTR + (ASC ? 1 : 0) + 2 * BCH + (FP4 || FP8 ? 2 : 0);   // loads per stage per thread
 
   f32x16 acc[MS][2];
 #pragma unroll
@@ -362,7 +388,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
       // (fp4: a wave without columns computes on its clamped rows and stores
       // nothing, with no branch around the accumulators)
       if (!FP4 && !wave_on) continue;
-      const uint8_t* Ab = As[buf];
+      const uint8_t* Ab = As(buf);
       if constexpr (BF16) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -408,7 +434,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
           }
         }
       } else if constexpr (FP8) {
-        const float sb0 = bscale_fp8(0, (kb + kt) * KS), sb1 = bscale_fp8(1, (kb + kt) * KS);
+        const float sb0 = sbf[buf][0], sb1 = sbf[buf][1];
 #pragma unroll
         for (int i = 0; i < MS; ++i) {
           if (i >= act_ms) continue;
@@ -657,7 +683,7 @@ static void rs_launch_t(int ms, dim3 grid, const GemmArgs& g, hipStream_t st) {
 // library built with MOE_FORCE_FLAT_COPIES=1 always takes the FLAT form.
 template <int MODE, int RECIPE>
 static void rs_launch(int ms, dim3 grid, const GemmArgs& g, hipStream_t st) {
-  if constexpr (RECIPE == MOE_RECIPE_MXFP4 || RECIPE == MOE_RECIPE_NVFP4) {
+  if constexpr (RECIPE == MOE_RECIPE_MXFP4 || RECIPE == MOE_RECIPE_NVFP4 || RECIPE == MOE_RECIPE_FP8_B128) {
     constexpr int64_t ea = RECIPE == MOE_RECIPE_NVFP4 ? 2 : 1;
     if (!MOE_FORCE_FLAT_COPIES && g.a_rows > 0 && g.a_rows * g.lda * ea < (int64_t(1) << 32) - 256) {
       rs_launch_t<MODE, RECIPE, true>(ms, grid, g, st);
