@@ -53,6 +53,30 @@ def test_e2m1_encoder_ties_to_even():
     assert list(vals) == [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, 0.0, -4.0, 6.0, 0.0, 6.0]
 
 
+def test_zipf_bias_load_follows_its_target_shares():
+    """The skewed workload's realised per-expert load (oracle routing, full hidden
+    size, 4096 tokens) against the Zipf(1.1) targets the bias was drawn for: the
+    rank-1 expert sees (nearly) every token, loads rank the experts as the target
+    does, the head falls off as rank^-s, and ranks 2..20 take their target share
+    to within -30% / +50%."""
+    from scipy.stats import spearmanr
+    cfg = C.SKEWED_FP8.replace(num_tokens=4096)
+    inp = G.generate(cfg, experts=False)
+    r = O.route(cfg, inp.x.float().double().numpy(), inp.gate_w.double().numpy(), inp.bias.numpy())
+    load = np.bincount(r["idx"].reshape(-1), minlength=cfg.num_experts)
+    rank, q = G.zipf_target(cfg)
+    rank, q = rank.numpy(), q.numpy()
+    order = np.argsort(rank)
+    T = cfg.num_tokens
+    assert load[order[0]] >= 0.95 * T
+    assert spearmanr(load, -rank).correlation >= 0.85
+    rr = np.arange(2, 51)
+    slope = np.polyfit(np.log(rr), np.log(np.maximum(load[order[rr - 1]], 1)), 1)[0]
+    assert -cfg.bias_param - 0.25 <= slope <= -cfg.bias_param + 0.25, slope
+    ratio = (load / T) / q
+    assert np.all((ratio[order[1:20]] >= 0.7) & (ratio[order[1:20]] <= 1.5)), ratio[order[1:20]]
+
+
 def test_zipf_bias_gives_heavy_tailed_load():
     cfg = C.SKEWED_FP8.replace(num_tokens=2048, hidden=256, gate_std=1.0 / 16)
     inp = G.generate(cfg, experts=False)

@@ -125,15 +125,10 @@ def encode_mxfp4(w: torch.Tensor):
 
 
 # ---------------------------------------------------------------- bias for skewed load
-def zipf_bias(cfg: C.MoEConfig, key_spread: float = 0.5) -> torch.Tensor:
-    """Bias whose induced load is heavy-tailed, approximately Zipf(s) over a seeded expert ranking.
-
-    Surrogate model (not the layer's scoring): each (token, expert) key is
-    z + b_e with z ~ N(0, key_spread^2) i.i.d.; then expert e is picked with
-    probability Phi(b_e / key_spread) at threshold 0.  Target pick probabilities
-    q_e = k * p_rank(e), p_r proportional to r^-s, water-filled under a cap of
-    0.995 so that sum q_e = k.  The realised loads are measured, not assumed.
-    """
+def zipf_target(cfg: C.MoEConfig):
+    """The seeded expert ranking (1 = most loaded) and the target pick probabilities
+    q_e = k * p_rank(e), p_r proportional to r^-s, water-filled under a cap of 0.995
+    so that sum q_e = k (float64 tensors [E])."""
     E, k, s = cfg.num_experts, cfg.top_k, cfg.bias_param
     g = torch.Generator().manual_seed(tensor_seed(cfg, "zipf_perm"))
     perm = torch.randperm(E, generator=g)
@@ -153,7 +148,20 @@ def zipf_bias(cfg: C.MoEConfig, key_spread: float = 0.5) -> torch.Tensor:
         rest = k - cap * fixed.sum()
         free = ~fixed
         q[free] = p[free] / p[free].sum() * rest
-    b = key_spread * torch.special.ndtri(q.clamp(1e-6, cap))
+    return rank, q
+
+
+def zipf_bias(cfg: C.MoEConfig, key_spread: float = 0.5) -> torch.Tensor:
+    """Bias whose induced load is heavy-tailed, approximately Zipf(s) over a seeded expert ranking.
+
+    Surrogate model (not the layer's scoring): each (token, expert) key is
+    z + b_e with z ~ N(0, key_spread^2) i.i.d.; then expert e is picked with
+    probability Phi(b_e / key_spread) at threshold 0, and b_e is chosen so that
+    this is the target q_e of zipf_target.  The realised loads are measured, not
+    assumed.
+    """
+    _, q = zipf_target(cfg)
+    b = key_spread * torch.special.ndtri(q.clamp(1e-6, 0.995))
     return b.to(torch.float32)
 
 
