@@ -44,6 +44,7 @@ struct FfnScratch {
 struct FfnPlan {
   bool f32;              // fp32 recipe: VALU kernel, 16-row tiles (list S only)
   int thresh;            // experts with >= thresh rows go to list L
+  bool nt;               // list L's weight copies take the non-temporal cache policy
   int bm_l, bm_s;        // rows per tile of each list
   int max_l, max_s;      // grid bounds of each list
 };
