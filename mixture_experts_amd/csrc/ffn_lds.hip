@@ -171,9 +171,9 @@ __device__ __forceinline__ void stage_fp8(f32x4 (&acc)[MU][NC], const uint8_t* A
   f32x4 part[NC];
   float sa[MU];
 #pragma unroll
-  for (int q = 0; q < MU / 4; ++q) {
-    const float4 v = *reinterpret_cast<const float4*>(Sp + (wm * 16 + r16) * MU + 4 * q);
-    sa[4 * q] = v.x; sa[4 * q + 1] = v.y; sa[4 * q + 2] = v.z; sa[4 * q + 3] = v.w;
+  for (int q = 0; q < MU / 2; ++q) {            // (MU * 4 bytes per lane: 8-byte aligned)
+    const float2 v = *reinterpret_cast<const float2*>(Sp + (wm * 16 + r16) * MU + 2 * q);
+    sa[2 * q] = v.x; sa[2 * q + 1] = v.y;
   }
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -338,16 +338,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
     const int r = tid % BM, i = r >> 5;
     sa_pos = ((i % WM) * 16 + (r & 15)) * (2 * MW) + 2 * (i / WM) + ((r >> 4) & 1);
   }
-  auto issue = [&](int k0, int buf) {
-    // (a copy whose 8 rows all lie past the tile's real rows is skipped: its LDS
-    // rows only feed accumulator rows that are never stored)
-#pragma unroll
-    for (int j = 0; j < A_INSTR; ++j)
-      if ((wave * A_INSTR + j) * (1024 / ROWB) < ti.rows)
-        copy_a(j, k0, As(buf) + (wave * A_INSTR + j) * 1024);
-    const size_t ko = koff_bytes(k0);
-#pragma unroll
-    for (int j = 0; j < B_INSTR; ++j) copy_b(j, ko, Bs(buf) + (wave * B_INSTR + j) * 1024);
+  auto load_scales = [&](int k0, int buf) {
     if (FP8 && tid < BM) {
       const float* SA = static_cast<const float*>(g.A_scale);
       sa_reg[buf] = SA[size_t(sa_row) * (K / 128) + k0 / 128];
@@ -364,6 +355,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
         sb_reg[buf] = SB[(size_t(sub) * (g.N / 128) + cb) * (ns / 128) + (k0 % ns) / 128];
       }
     }
+  };
+  auto issue = [&](int k0, int buf) {
+    // (a copy whose 8 rows all lie past the tile's real rows is skipped: its LDS
+    // rows only feed accumulator rows that are never stored)
+#pragma unroll
+    for (int j = 0; j < A_INSTR; ++j)
+      if ((wave * A_INSTR + j) * (1024 / ROWB) < ti.rows)
+        copy_a(j, k0, As(buf) + (wave * A_INSTR + j) * 1024);
+    const size_t ko = koff_bytes(k0);
+#pragma unroll
+    for (int j = 0; j < B_INSTR; ++j) copy_b(j, ko, Bs(buf) + (wave * B_INSTR + j) * 1024);
+    load_scales(k0, buf);
   };
 
   // Tile-relative weight column of each of this wave's fragments (SwiGLU: the h
@@ -522,6 +525,100 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
     else if (MW >= 2 && nj == 2) mainloop(std::integral_constant<int, (MW >= 2 ? 2 : 0)>{});
     else if (nj == 1) mainloop(std::integral_constant<int, 1>{});
     else mainloop(std::integral_constant<int, 0>{});
+  } else if constexpr (PIPE == 3 && FP8) {
+    // ---- fp8 main loop, activation (and scale) ring of 2 slots, weight ring of 3:
+    // stage kt reads A / scale slot kt % 2 and B slot kt % 3.  At the top of stage
+    // kt a wave waits, by count, for its own copies of stage kt while stage kt+1's
+    // weights (issued last) stay in flight; after the barrier it refills the slots
+    // stage kt-1 has finished with: stage kt+1's activations and scales, then stage
+    // kt+2's weights.  The weight copies thus have two stages of compute to land.
+    uint8_t* const Bs2 = lds_wslot2<NB * ROWB>();
+    auto Asl = [&](auto ac) -> uint8_t* { return decltype(ac)::value == 0 ? As0 : As1; };
+    auto Bsl = [&](auto bc) -> uint8_t* {
+      return decltype(bc)::value == 0 ? Bs0 : (decltype(bc)::value == 1 ? Bs1 : Bs2);
+    };
+    // Activation copies, then the stage's scales.  Unlike the other loops, every
+    // copy is issued, also those of rows past the tile's last real row (they read
+    // that row again): with the copies under a branch, the compiler no longer
+    // tells their LDS slot from the one being read and makes each stage wait for
+    // the next stage's activations before its first LDS read.
+    auto issue_a = [&](int k0, auto ac) {
+      constexpr int a = decltype(ac)::value;
+#pragma unroll
+      for (int j = 0; j < A_INSTR; ++j) copy_a(j, k0, Asl(ac) + (wave * A_INSTR + j) * 1024);
+      load_scales(k0, a);
+    };
+    auto issue_b = [&](int k0, auto bc) {          // B_INSTR copies per wave, always
+      const size_t ko = koff_bytes(k0);
+#pragma unroll
+      for (int j = 0; j < B_INSTR; ++j) copy_b(j, ko, Bsl(bc) + (wave * B_INSTR + j) * 1024);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    const int r16 = lane & 15, kg = lane >> 4;
+    constexpr int MU = 2 * MW, NC = 2 * NF;
+    // FULL: the steady state, where stages kt+1 and kt+2 exist and the copies are
+    // issued without a branch.  (With a branch around them, the compiler's own
+    // wait before the scale writes can no longer count the weight copies that
+    // follow the scale loads on every path, and it waits for all of them.)
+    auto step = [&](auto fullc, int kt, auto ac, auto bc) {
+      constexpr bool FULL = decltype(fullc)::value;
+      constexpr int a = decltype(ac)::value, b = decltype(bc)::value;
+      if (FULL || kt + 1 < KT) wait_vmcnt<B_INSTR>();   // all but stage kt+1's weights
+      else wait_vmcnt<0>();
+      float* const sa_l = a == 0 ? Sa0 : Sa1;
+      float* const sb_l = a == 0 ? Sb0 : Sb1;
+      if (tid < BM) sa_l[sa_pos] = sa_reg[a];
+      if (tid < 2) sb_l[tid] = sb_reg[a];
+      lds_barrier();                                // everyone's stage kt landed; stage kt-1 read
+      // (scheduling barriers keep the issue order: the scale loads must precede
+      // the weight copies that the next stage's wait leaves in flight)
+      sched_fence();
+      if (FULL || kt + 1 < KT) issue_a((kt + 1) * KS, std::integral_constant<int, a ^ 1>{});
+      sched_fence();
+      if (FULL || kt + 2 < KT) issue_b((kt + 2) * KS, std::integral_constant<int, (b + 2) % 3>{});
+      sched_fence();
+      const float sbv[2] = {sb_l[0], sb_l[1]};
+      const uint8_t* Ab = Asl(ac);
+      const uint8_t* Bw = Bsl(bc) + brow0 * ROWB;
+      // (the row-fragment count is dispatched here, inside the step: one loop per
+      // count made the compiler move the units' MFMAs together and spill)
+      if (MW >= 4 && nj == 4) stage_fp8<(MW >= 4 ? 8 : 2), MU, NC, WM, SPLIT, NB>(acc4, Ab, Bw, sa_l, sbv, sbi, wm, r16, kg);
+      else if (MW >= 3 && nj == 3) stage_fp8<(MW >= 3 ? 6 : 2), MU, NC, WM, SPLIT, NB>(acc4, Ab, Bw, sa_l, sbv, sbi, wm, r16, kg);
+      else if (MW >= 2 && nj == 2) stage_fp8<(MW >= 2 ? 4 : 2), MU, NC, WM, SPLIT, NB>(acc4, Ab, Bw, sa_l, sbv, sbi, wm, r16, kg);
+      else if (nj == 1) stage_fp8<2, MU, NC, WM, SPLIT, NB>(acc4, Ab, Bw, sa_l, sbv, sbi, wm, r16, kg);
+    };
+    using F = std::true_type;
+    using T = std::false_type;
+    issue_a(0, I0{});
+    sched_fence();
+    issue_b(0, I0{});
+    if (KT == 1) {
+      sched_fence();
+      step(T{}, 0, I0{}, I0{});
+    } else {
+      // (stage 1's weights issued on every path into the loop, so that the
+      // compiler's count of the copies in flight is the same on all of them)
+      issue_b(KS, I1{});
+      sched_fence();
+      int kt = 0;
+      for (; kt + 7 < KT; kt += 6) {
+        step(F{}, kt, I0{}, I0{});
+        step(F{}, kt + 1, I1{}, I1{});
+        step(F{}, kt + 2, I0{}, I2{});
+        step(F{}, kt + 3, I1{}, I0{});
+        step(F{}, kt + 4, I0{}, I1{});
+        step(F{}, kt + 5, I1{}, I2{});
+      }
+      step(T{}, kt, I0{}, I0{});                      // the last 2..7 stages
+      step(T{}, kt + 1, I1{}, I1{});
+      if (kt + 2 < KT) step(T{}, kt + 2, I0{}, I2{});
+      if (kt + 3 < KT) step(T{}, kt + 3, I1{}, I0{});
+      if (kt + 4 < KT) step(T{}, kt + 4, I0{}, I1{});
+      if (kt + 5 < KT) step(T{}, kt + 5, I1{}, I2{});
+      if (kt + 6 < KT) step(T{}, kt + 6, I0{}, I0{});
+    }
   } else {
   // ---- main loop: stage kt is consumed from slot kt % NST while stage kt+1 lands
 #pragma unroll
@@ -669,7 +766,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
 
 template <int MS, int MODE, int KIND, bool BUF, int WM, int WN, int PIPE = 0, int NB = 256, bool NTB = false>
 void launch_lds_variant(const GemmArgs& g, int m_tiles, hipStream_t st) {
-  constexpr size_t lds = size_t(NST) * (MS * 32 + NB) * ROWB + (PIPE == 2 ? size_t(NB) * ROWB : 0) +
+  constexpr size_t lds = size_t(NST) * (MS * 32 + NB) * ROWB + (PIPE >= 2 ? size_t(NB) * ROWB : 0) +
                          (KIND == KIND_FP8 ? size_t(NST + WN) * MS * 32 * 4 + 32 : 0);
   static_assert(lds <= 160 * 1024, "LDS budget");
   const int ncols = (MODE == EPI_SWIGLU) ? g.N / (NB / 2) : (g.N + NB - 1) / NB;
@@ -683,9 +780,9 @@ void launch_lds_variant(const GemmArgs& g, int m_tiles, hipStream_t st) {
 // nt (bf16): non-temporal weight copies (see ffn_lds_kernel's NTB).
 template <int MODE, int KIND, bool BUF>
 static hipError_t launch_lds_tiles(int m_tiles, const GemmArgs& g, bool nt, hipStream_t st) {
-  if constexpr (KIND == KIND_FP8) launch_lds_variant<8, MODE, KIND, BUF, 2, 4>(g, m_tiles, st);
-  else if (nt) launch_lds_variant<8, MODE, KIND, BUF, 2, 4, 2, 256, true>(g, m_tiles, st);
-  else launch_lds_variant<8, MODE, KIND, BUF, 2, 4, 2>(g, m_tiles, st);
+  if constexpr (KIND == KIND_FP8) launch_lds_variant<LDS_ROWS_FP8 / 32, MODE, KIND, BUF, 2, 4, 3>(g, m_tiles, st);
+  else if (nt) launch_lds_variant<LDS_ROWS_BF16 / 32, MODE, KIND, BUF, 2, 4, 2, 256, true>(g, m_tiles, st);
+  else launch_lds_variant<LDS_ROWS_BF16 / 32, MODE, KIND, BUF, 2, 4, 2>(g, m_tiles, st);
   return hipGetLastError();
 }
 

@@ -40,6 +40,11 @@ struct FfnScratch {
   void* h_scale;         // fp32 [T*k][I/128] or E8M0 [T*k][I/32]
 };
 
+// Rows per tile of the LDS-staged kernel: bf16 256; fp8 192, whose smaller
+// activation slots leave room in LDS for a third weight slot.
+constexpr int LDS_ROWS_BF16 = 256;
+constexpr int LDS_ROWS_FP8 = 192;
+
 // How the routed experts' rows are cut into tiles and which kernel runs them.
 struct FfnPlan {
   bool f32;              // fp32 recipe: VALU kernel, 16-row tiles (list S only)

@@ -195,7 +195,7 @@ FfnPlan ffn_plan(const moe_config_t& c) {
   // weights are read once); measured 4.93 -> 4.39 ms per bf16 decode step.
   p.nt = c.recipe == MOE_RECIPE_BF16 && avg <= 48;
   p.thresh = fp4w ? INT32_MAX : (p.nt ? 1 : 128);
-  p.bm_l = 256;
+  p.bm_l = c.recipe == MOE_RECIPE_FP8_B128 ? LDS_ROWS_FP8 : LDS_ROWS_BF16;
   p.max_l = (p.thresh == INT32_MAX || P < p.thresh) ? 0 : int((P + p.bm_l - 1) / p.bm_l + std::min<int64_t>(E, P / p.thresh));
   const int64_t small_bound = (p.thresh == INT32_MAX) ? (P + p.bm_s - 1) / p.bm_s + E
                                                       : E * ((p.thresh + p.bm_s - 1) / p.bm_s);
