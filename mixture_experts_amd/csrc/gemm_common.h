@@ -45,6 +45,9 @@ struct GemmArgs {
   const int32_t* pair_pos;
   const float* topk_w;
   int topk;
+  // LDS-staged kernel: > 1 numbers its tiles in groups of tile_group row tiles,
+  // row tile fastest within a group (see ffn_lds_kernel); else column tile fastest
+  int tile_group;
 };
 
 struct TileInfo {

@@ -52,6 +52,7 @@ struct FfnPlan {
   bool nt;               // list L's weight copies take the non-temporal cache policy
   int bm_l, bm_s;        // rows per tile of each list
   int max_l, max_s;      // grid bounds of each list
+  int tile_group;        // list L's tile order (GemmArgs::tile_group)
 };
 FfnPlan ffn_plan(const moe_config_t& c);
 

@@ -152,7 +152,7 @@ def test_more_shapes(cfg):
 # fit 4 GiB, else with 64-bit FLAT copies.  No test shape reaches the second form,
 # so these cases run the library build that forces it (libmoe_mi355x_flatcopy.so).
 @pytest.mark.parametrize("cfg", [C.MINI_PREFILL_BF16, C.MINI_PREFILL_FP8, C.MINI_MIXED_BF16, C.MINI_MXFP4_WIDE,
-                                 C.MINI_NVFP4], ids=lambda c: c.name)
+                                 C.MINI_NVFP4, C.MINI_SKEWED_FP8], ids=lambda c: c.name)
 def test_lds_flat_copy_form(cfg):
     import mixture_experts_amd as M
     with M.library(M.FLAT_LIB_PATH):

@@ -169,8 +169,16 @@ MINI_NVFP4_WIDE = MoEConfig(
     recipe=RECIPE_NVFP4, gate_std=1.0 / 16.0,
     description="NVFP4 mini with about 140 rows per expert: 128-row tiles")
 
+MINI_SKEWED_FP8 = MoEConfig(
+    name="mini_skewed_fp8", num_tokens=1200, hidden=384, num_experts=12, top_k=2,
+    intermediate=256, num_shared=1, shared_intermediate=128,
+    score_func=SCORE_SQRTSOFTPLUS, routed_scaling_factor=2.5, recipe=RECIPE_FP8_B128,
+    gate_std=1.0 / 16.0, bias_kind="zipf", bias_param=1.1,
+    description="fp8 mini averaging 200 rows per expert with a Zipf load: heavy experts of several "
+                "192-row tiles, run in groups of row tiles")
+
 MINI_CONFIGS = [MINI_GROUPED_BF16, MINI_DECODE_BF16, MINI_MXFP4, MINI_FP8, MINI_F32, MINI_PREFILL_BF16,
-                MINI_PREFILL_FP8, MINI_MXFP4_WIDE, MINI_MIXED_BF16, MINI_NVFP4, MINI_NVFP4_WIDE]
+                MINI_PREFILL_FP8, MINI_MXFP4_WIDE, MINI_MIXED_BF16, MINI_NVFP4, MINI_NVFP4_WIDE, MINI_SKEWED_FP8]
 
 # NVFP4 (walk-through section 4): the decode shape of the Kimi-K2-Thinking-NVFP4 /
 # DeepSeek-V3 layer with NVFP4 routed experts; not one of the five workloads above.
