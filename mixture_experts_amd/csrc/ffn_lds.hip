@@ -12,8 +12,9 @@
 //
 // Both operands are staged through LDS with gfx950's direct global->LDS 16-byte
 // loads into rings of 128-byte rows (64 bf16 or 128 fp8 of K per stage; whole
-// cache lines per row): two slots per operand, and for the 256-row bf16 tiles a
-// third weight slot, so that the weight copies run two stages ahead.  The copies
+// cache lines per row): two activation slots and three weight slots, so that the
+// weight copies run two stages ahead (tiles of 256 rows for bf16, 192 for fp8,
+// whose scale slots leave no room for the third weight slot at 256 rows).  The copies
 // use the buffer-descriptor form (buffer_load_dwordx4 ... lds, 32-bit offsets)
 // when the tensors allow it: while a FLAT-form copy (global_load_lds_dwordx4) is
 // outstanding, the compiler cannot order the LDS fragment reads against it and
@@ -33,11 +34,14 @@
 // (stage sum x row scale x weight scale, both staged through LDS with the
 // operands).
 //
-// Tiles are numbered (row tile, column tile), column tile fastest, and mapped so
-// that consecutive numbers run on the same XCD: the column tiles sharing an
-// activation block meet in that XCD's L2.  The row tiles of one expert read the
-// same weight rows, but far apart in time, so each of them streams the weights
-// from HBM again; experts of 257..511 rows therefore pay two weight passes.
+// Tiles are numbered (row tile, column tile) and mapped so that consecutive
+// numbers run on the same XCD: column tile fastest, so that the column tiles
+// sharing an activation block meet in that XCD's L2; or, when experts span many
+// row tiles, in groups of 8 row tiles with row tile fastest (GemmArgs::
+// tile_group), so that the row tiles of a heavy expert also share its weight
+// blocks.  With the first order the row tiles of one expert read the same weight
+// rows far apart in time, so each of them streams the weights from HBM again;
+// experts of 257..511 rows pay two weight passes.
 #include "gemm_common.h"
 #include "kernels.h"
 
@@ -121,37 +125,6 @@ __device__ __forceinline__ uint8_t* lds_wslot2() {
 // wave has already waited, by count, for the copies the next stage needs.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// One bf16 stage (64 K) for the NJ row fragments of this wave that hold real rows,
-// in 16-deep sub-steps: the operands of sub-step s+1 are read from LDS while the
-// MFMAs of sub-step s run (register double buffer; the order is pinned with
-// scheduling barriers).  Every LDS row a wave reads is 32*m + l32, whose swizzle
-// key is l32's.  Aw / Bw: the wave's first A / weight row in this stage's slot.
-template <int NJ, int MW, int NF, int WM, int SPLIT, int NB>
-__device__ __forceinline__ void stage_bf16(f32x16 (&acc)[MW][NF], const uint8_t* Aw, const uint8_t* Bw, int l32,
-                                           int half) {
-  constexpr int NS = ROWB / 32;
-  bf16x8 bv[2][NF], av[2][NJ];
-  auto rd = [&](int s, int slot) {
-    const int off = l32 * ROWB + (swz_slot(l32, 2 * s + half) << 4);   // k = 16s + 8h .. +8
-#pragma unroll
-    for (int f = 0; f < NF; ++f) bv[slot][f] = __builtin_bit_cast(bf16x8, lds16(Bw + bfrag_row<SPLIT, NB>(f) * ROWB + off));
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) av[slot][j] = __builtin_bit_cast(bf16x8, lds16(Aw + WM * 32 * ROWB * j + off));
-  };
-  rd(0, 0);
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    if (s + 1 < NS) rd(s + 1, (s + 1) & 1);
-    sched_fence();
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-        acc[j][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[s & 1][f], av[s & 1][j], acc[j][f], 0, 0, 0);
-    sched_fence();
-  }
-}
-
 // One fp8 stage (128 K, one 128-block of both scale grids) for the NU 16-row
 // blocks of this wave that hold real rows.  Row block u: rows
 // (wm + WM*(u>>1))*32 + 16*(u&1) + 0..15; column block c = 2f + cb: weight
@@ -210,12 +183,13 @@ __device__ __forceinline__ void stage_fp8(f32x4 (&acc)[MU][NC], const uint8_t* A
   }
 }
 
-// MS: 32-row fragments per tile; WM x WN: wavefront grid; PIPE (bf16 only): 2 =
-// the stage barrier sits before the stage's last sub-step, so that stage k+2's
-// copies and stage k+1's first LDS reads overlap stage k's last MFMAs, with three
-// weight slots (and two activation slots), so that each stage's weight copies
-// have two stages of compute to land; 0 = one stage in flight (fp8); NB: weight
-// rows per tile (SwiGLU: NB/2 h columns).  NTB: the weight copies take the
+// MS: 32-row fragments per tile; WM x WN: wavefront grid; PIPE: the main loop,
+// both with two activation slots and three weight slots, so that each stage's
+// weight copies have two stages of compute to land -- 2 (bf16): the stage
+// barrier sits before the stage's last sub-step, so that stage k+2's copies and
+// stage k+1's first LDS reads overlap stage k's last MFMAs; 3 (fp8): the barrier
+// at the stage start, the scales staged with the activations; NB: weight rows
+// per tile (SwiGLU: NB/2 h columns).  NTB: the weight copies take the
 // non-temporal cache policy, for launches in which each expert's weights are
 // read by one row tile only (nothing later reuses them from L2 or the MALL):
 // full-line non-temporal reads streamed at 7.1 TB/s on the box against 6.3 for
@@ -250,10 +224,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
     Sb1 = lds_f32<4, 3>();
     amax_lds = lds_f32<WN * BM, 4>();                // epilogue
   }
-  auto As = [&](int buf) -> uint8_t* { return buf == 0 ? As0 : As1; };
-  auto Bs = [&](int buf) -> uint8_t* { return buf == 0 ? Bs0 : Bs1; };
-  auto Sa = [&](int buf) -> float* { return buf == 0 ? Sa0 : Sa1; };
-  auto Sb = [&](int buf) -> float* { return buf == 0 ? Sb0 : Sb1; };
 
   const int ncols = (MODE == EPI_SWIGLU) ? g.N / (NB / 2) : (g.N + NB - 1) / NB;
   const int V = ncols * row_tiles(g, BM);
@@ -372,19 +342,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
       }
     }
   };
-  auto issue = [&](int k0, int buf) {
-    // (a copy whose 8 rows all lie past the tile's real rows is skipped: its LDS
-    // rows only feed accumulator rows that are never stored)
-#pragma unroll
-    for (int j = 0; j < A_INSTR; ++j)
-      if ((wave * A_INSTR + j) * (1024 / ROWB) < ti.rows)
-        copy_a(j, k0, As(buf) + (wave * A_INSTR + j) * 1024);
-    const size_t ko = koff_bytes(k0);
-#pragma unroll
-    for (int j = 0; j < B_INSTR; ++j) copy_b(j, ko, Bs(buf) + (wave * B_INSTR + j) * 1024);
-    load_scales(k0, buf);
-  };
-
   // Tile-relative weight column of each of this wave's fragments (SwiGLU: the h
   // column block of the gate/up pair); the wave's first LDS weight row.
   int fcol[NF];
@@ -415,28 +372,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
   int sbi[NF];                                      // fp8: weight-scale index of fragment f
 #pragma unroll
   for (int f = 0; f < NF; ++f) sbi[f] = (MODE == EPI_SWIGLU) ? (f < NFG ? 0 : 1) : fcol[f] / 128;
-
-  auto compute = [&](int buf) {
-    const uint8_t* Bw = Bs(buf) + brow0 * ROWB;
-    if constexpr (!FP8) {
-      const int half = lane >> 5, l32 = lane & 31;
-      const uint8_t* Aw = As(buf) + wm * 32 * ROWB;
-      if (MW >= 4 && nj == 4) stage_bf16<(MW >= 4 ? 4 : 1), MW, NF, WM, SPLIT, NB>(acc16, Aw, Bw, l32, half);
-      else if (MW >= 3 && nj == 3) stage_bf16<(MW >= 3 ? 3 : 1), MW, NF, WM, SPLIT, NB>(acc16, Aw, Bw, l32, half);
-      else if (MW >= 2 && nj == 2) stage_bf16<(MW >= 2 ? 2 : 1), MW, NF, WM, SPLIT, NB>(acc16, Aw, Bw, l32, half);
-      else if (nj == 1) stage_bf16<1, MW, NF, WM, SPLIT, NB>(acc16, Aw, Bw, l32, half);
-    } else {
-      const int r16 = lane & 15, kg = lane >> 4;
-      const uint8_t* Ab = As(buf);
-      const float* Sp = Sa(buf);
-      const float sbv[2] = {Sb(buf)[0], Sb(buf)[1]};
-      constexpr int MU = 2 * MW, NC = 2 * NF;
-      if (MW >= 4 && nj == 4) stage_fp8<(MW >= 4 ? 8 : 2), MU, NC, WM, SPLIT, NB>(acc4, Ab, Bw, Sp, sbv, sbi, wm, r16, kg);
-      else if (MW >= 3 && nj == 3) stage_fp8<(MW >= 3 ? 6 : 2), MU, NC, WM, SPLIT, NB>(acc4, Ab, Bw, Sp, sbv, sbi, wm, r16, kg);
-      else if (MW >= 2 && nj == 2) stage_fp8<(MW >= 2 ? 4 : 2), MU, NC, WM, SPLIT, NB>(acc4, Ab, Bw, Sp, sbv, sbi, wm, r16, kg);
-      else if (nj == 1) stage_fp8<2, MU, NC, WM, SPLIT, NB>(acc4, Ab, Bw, Sp, sbv, sbi, wm, r16, kg);
-    }
-  };
 
   const int KT = K / KS;
   if constexpr (PIPE == 2 && !FP8) {
@@ -636,27 +571,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
       if (kt + 6 < KT) step(T{}, kt + 6, I0{}, I0{});
     }
   } else {
-  // ---- main loop: stage kt is consumed from slot kt % NST while stage kt+1 lands
-#pragma unroll
-  for (int s = 0; s < NST - 1; ++s)
-    if (s < KT) issue(s * KS, s);
-  for (int kt0 = 0; kt0 < KT; kt0 += NST) {
-#pragma unroll
-    for (int buf = 0; buf < NST; ++buf) {            // unrolled: the ring slot is a constant
-      const int kt = kt0 + buf;
-      if (kt >= KT) break;
-      wait_vmcnt<0>();                              // stage kt has landed (own copies)
-      if (FP8) {
-        if (tid < BM) Sa(buf)[sa_pos] = sa_reg[buf];
-        if (tid < 2) Sb(buf)[tid] = sb_reg[buf];
-      }
-      __syncthreads();
-      // refill the slot consumed in the previous iteration
-      const int nb = (buf + NST - 1) % NST;
-      if (kt + NST - 1 < KT) issue((kt + NST - 1) * KS, nb);
-      compute(buf);
-    }
-  }
+    static_assert(PIPE == 2 || PIPE == 3, "bf16 runs the PIPE 2 loop, fp8 the PIPE 3 loop");
   }
 
   // ---- epilogues
