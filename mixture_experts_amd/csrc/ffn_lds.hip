@@ -230,23 +230,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_lds_kernel(GemmArgs g) {
   const int b = blockIdx.y * gridDim.x + blockIdx.x;
   if (b >= V) return;
   const int tnum = xcd_tile(b, V);
-  // g.tile_group = GM > 1: tile numbers come in groups of GM row tiles x all
-  // column tiles, row tile fastest within a group, so that the ~32 workgroups an
-  // XCD holds at once cover GM row tiles x a few column tiles and share weight and
-  // activation blocks in L2 (for launches whose experts span several row tiles).
-  // Otherwise column tile fastest: the column tiles of a row tile share its
-  // activations.
+  // g.tile_group > 1 (launches whose experts span several row tiles): the ~32
+  // workgroups an XCD holds at once cover tile_group row tiles x a few column
+  // tiles and share weight and activation blocks in L2; otherwise column tile
+  // fastest, so that the column tiles of a row tile share its activations.
   int mt, nt;
-  if (g.tile_group > 1) {
-    const int GM = g.tile_group;
-    const int nrt = V / ncols, gr0 = tnum / (GM * ncols) * GM;
-    const int gsz = min(GM, nrt - gr0), idx = tnum - gr0 * ncols;
-    mt = gr0 + idx % gsz;
-    nt = idx / gsz;
-  } else {
-    mt = tnum / ncols;
-    nt = tnum - mt * ncols;
-  }
+  tile_coords(tnum, V, ncols, g.tile_group, mt, nt);
   TileInfo ti;
   tile_info(g, BM, mt, ti);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;

@@ -83,9 +83,25 @@ __device__ __forceinline__ int row_tiles(const GemmArgs& g, int BM) {
 // Bijective map of a linear block index b < V to a tile number so that the blocks
 // one XCD runs (b % 8 fixed: workgroups are dealt round-robin over the eight XCDs)
 // cover a contiguous range of tile numbers and share that XCD's L2.
-__device__ __forceinline__ int xcd_tile(int b, int V) {
+__host__ __device__ __forceinline__ int xcd_tile(int b, int V) {
   const int q = V >> 3, r = V & 7, x = b & 7, l = b >> 3;
   return (x < r) ? x * (q + 1) + l : r * (q + 1) + (x - r) * q + l;
+}
+
+// (row tile mt, column tile nt) of tile number tnum < V = row tiles x ncols.
+// group > 1: the numbers come in groups of `group` row tiles x all ncols column
+// tiles, row tile fastest within a group (the last group may hold fewer row
+// tiles); else column tile fastest.  A bijection either way.
+__host__ __device__ __forceinline__ void tile_coords(int tnum, int V, int ncols, int group, int& mt, int& nt) {
+  if (group > 1) {
+    const int nrt = V / ncols, gr0 = tnum / (group * ncols) * group;
+    const int gsz = (group < nrt - gr0) ? group : nrt - gr0, idx = tnum - gr0 * ncols;
+    mt = gr0 + idx % gsz;
+    nt = idx / gsz;
+  } else {
+    mt = tnum / ncols;
+    nt = tnum - mt * ncols;
+  }
 }
 
 // A-operand row of pair row p (see GemmArgs::a_map).

@@ -5,7 +5,8 @@
 //   - the tile-list bounds that size the workspace: the counts the device
 //     builder writes, for adversarial per-expert row counts, stay within them;
 //   - argument validation: each entry point's error for each bad argument,
-//     returned before anything is enqueued.
+//     returned before anything is enqueued;
+//   - the GEMM kernels' block -> tile map (xcd_tile, tile_coords) is a bijection.
 // The translation unit includes the library's API source, so its internal layout
 // and plan functions are the ones under test.
 #include "../../mixture_experts_amd/csrc/moe_api.hip"
@@ -126,6 +127,29 @@ void check_layout(const moe_config_t& c, std::mt19937_64& rng) {
   }
 }
 
+// The GEMM kernels' block -> tile map: xcd_tile, then tile_coords, must hit every
+// (row tile, column tile) once, for every group size the host picks and ragged
+// row-tile counts (a last group with fewer row tiles).
+void check_tile_map() {
+  for (int ncols : {1, 2, 8, 16, 28, 32, 56})
+    for (int nrt = 1; nrt <= 70; ++nrt)
+      for (int group : {0, 2, 8}) {
+        const int V = nrt * ncols;
+        std::vector<int> seen(size_t(V), 0);
+        bool ok = true;
+        for (int b = 0; b < V; ++b) {
+          const int t = xcd_tile(b, V);
+          int mt = -1, nt = -1;
+          if (t < 0 || t >= V) { ok = false; break; }
+          tile_coords(t, V, ncols, group, mt, nt);
+          if (mt < 0 || mt >= nrt || nt < 0 || nt >= ncols) { ok = false; break; }
+          ++seen[size_t(mt) * ncols + nt];
+        }
+        for (int v : seen) ok = ok && v == 1;
+        CHECK(ok, "ncols=%d row tiles=%d group=%d", ncols, nrt, group);
+      }
+}
+
 void check_validation() {
   moe_config_t c = make(64, 256, 16, 4, 128, 1, 128, 1, 1, MOE_RECIPE_F32);
   alignas(256) static char ws_small[256];
@@ -184,6 +208,7 @@ int main() {
     check_layout(make(4096, 7168, 896, 16, 1024, 2, 1024, 1, 1, rc), rng);
   }
   check_validation();
+  check_tile_map();
   std::printf("host checks: %d failures\n", failures);
   return failures ? 1 : 0;
 }
